@@ -1,0 +1,178 @@
+"""Benchmark of the fused FP8 MoE expert layer on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|mid|prefill|wide|tiny]
+
+A step is one forward of the whole layer (dispatch, the persistent expert
+kernel, combine) over one batch of seeded synthetic inputs already resident in
+HBM.  Prints one JSON line.  The default workload is the 128-token decode
+batch (hidden 7168, intermediate 2048, 32 local experts, top-8, uniform
+routing), which is weight-stream bound: ``value`` is the achieved
+weight-stream rate (bytes of the active experts' FP8 weights and scales per
+step / step time); the prefill workload reports FP8 TFLOP/s instead.
+
+``roofline`` describes the dominant kernel (the persistent expert kernel),
+timed with HIP events recorded around it on its own stream during the timed
+steps; its algorithmic bytes and FLOPs per launch are computed below.
+``cpu_baseline`` times the float64 CPU oracle on this host on a bounded sample
+of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 matrix peak
+METRIC = "MoE layer FP8 TFLOPS & weight-stream HBM GB/s (decode/prefill), % roofline"
+
+
+def work_of(inp):
+    """Algorithmic work of one step (routing-dependent, exact for these inputs)."""
+    x, idx = inp["x"], inp["topk_idx"]
+    T, H = x.shape
+    E, N, _ = inp["w1"].shape
+    I = N // 2
+    k = idx.shape[1]
+    act = (idx >= 0) & (idx < E)
+    R = int(act.sum())
+    active_experts = int(len(np.unique(idx[act])))
+    flops = 6.0 * H * I * R
+    w_bytes = active_experts * (3.0 * H * I + 4.0 * (2 * I // 128) * (H // 128)
+                                + 4.0 * (H // 128) * (I // 128))
+    io_bytes = T * H + 4.0 * T * (H // 128) + 8.0 * T * k + 2.0 * T * H
+    # the expert kernel: weights + pool rows and scales in, re-quantised
+    # activations out and back in, BF16 partials out
+    route_bytes = H + 4.0 * (H // 128) + 4 + 2.0 * (I + 4.0 * (I // 64)) + 2.0 * H
+    return dict(T=T, H=H, I=I, E=E, k=k, R=R, active_experts=active_experts, flops=flops,
+                weight_bytes=w_bytes, compulsory_bytes=w_bytes + io_bytes,
+                expert_kernel_bytes=w_bytes + R * route_bytes)
+
+
+def cpu_baseline(name, inp, work):
+    """Time the oracle on a bounded sample of the workload on this host."""
+    from oracle import moe
+    cores = len(os.sched_getaffinity(0))
+    T = inp["x"].shape[0]
+    if T <= 128:
+        t0 = time.perf_counter()
+        moe.forward(inp)
+        dt = time.perf_counter() - t0
+        sample = f"full {name} workload ({T} tokens)"
+        frac = 1.0
+    else:
+        n = 64
+        toks = list(range(n))
+        t0 = time.perf_counter()
+        moe.forward_tokens(inp, toks)
+        dt = time.perf_counter() - t0
+        sample = f"first {n} of {T} tokens of the {name} workload, scaled by routes"
+        frac = float(((inp["topk_idx"][:n] >= 0) & (inp["topk_idx"][:n] < work["E"])).sum()) / work["R"]
+    if name == "prefill":
+        value, unit = work["flops"] * frac / dt / 1e12, "TFLOP/s"
+    else:
+        value, unit = work["weight_bytes"] / (dt / frac) / 1e9, "GB/s"
+    return {"value": value, "unit": unit, "cores": cores, "kind": "oracle", "sample": sample,
+            "seconds": dt, "blas": "numpy float64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--l2-n-major", type=int, default=-1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the layer is one GPU's share of expert "
+              f"parallelism; no multi-GPU path is built); got --gpus {args.gpus}", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from fp8_mixture_experts_amd import binding as B
+    from fp8_mixture_experts_amd import synthetic as S
+
+    name = args.workload
+    inp = S.make_inputs(name)
+    work = work_of(inp)
+    dev = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to("cuda:0")
+           for k in ("x", "x_sf", "topk_idx", "topk_weights", "w1", "w1_sf", "w2", "w2_sf")}
+    T, H = inp["x"].shape
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda:0")
+    layer = B.MegaMoE(work["E"], H, work["I"], work["k"], T, block_m=args.block_m,
+                      l2_n_major=args.l2_n_major)
+    plan = B.mega_moe_plan(layer.cfg, T)
+
+    def step():
+        layer.forward(dev["x"], dev["x_sf"], dev["topk_idx"], dev["topk_weights"], dev["w1"],
+                      dev["w1_sf"], dev["w2"], dev["w2_sf"], y)
+
+    for _ in range(args.warmup):
+        step()
+    status = layer.status()
+    if status:
+        raise SystemExit(f"device error bits {status:#x}")
+    torch.cuda.synchronize()
+    B.mega_moe_profile_begin(layer.handle, args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = B.mega_moe_profile_end(layer.handle, args.steps)
+    status = layer.status()
+    if status:
+        raise SystemExit(f"device error bits {status:#x}")
+    layer.close()
+
+    ms = (t1 - t0) * 1e3 / args.steps
+    s = ms / 1e3
+    k_ms = np.array(prof)                      # [steps, 3] dispatch / expert / combine
+    expert_ms = float(k_ms[:, 1].mean())
+    tflops = work["flops"] / s / 1e12
+    wgbs = work["weight_bytes"] / s / 1e9
+    t_roof = max(work["compulsory_bytes"] / (HBM_PEAK_GBS * 1e9), work["flops"] / (FP8_PEAK_TFLOPS * 1e12))
+    if name == "prefill":
+        value, unit = tflops, "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": work["flops"] / (expert_ms / 1e3) / 1e12,
+                "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        value, unit = wgbs, "GB/s"
+        roof = {"bound": "hbm", "achieved": work["expert_kernel_bytes"] / (expert_ms / 1e3) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = f"moe_expert_ffn<{plan.block_m}>"
+    roof["kernel_ms"] = expert_ms
+    out = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": name, "tokens": T, "hidden": H, "intermediate": work["I"],
+                   "experts": work["E"], "topk": work["k"], "routing": inp["workload"].routing,
+                   "block_m": plan.block_m, "l2_n_major": plan.l2_n_major},
+        "tflops": tflops, "weight_stream_gbs": wgbs,
+        "pct_roofline": 100.0 * t_roof / s,
+        "kernel_ms": {"dispatch": float(k_ms[:, 0].mean()), "expert": expert_ms,
+                      "combine": float(k_ms[:, 2].mean())},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(name, inp, work)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

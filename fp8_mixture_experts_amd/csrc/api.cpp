@@ -1,0 +1,379 @@
+// Host side of the C ABI declared in include/mega_moe.h: argument checks, the
+// per-call plan, workspace layout and the launches of the three kernel groups
+// (dispatch, persistent expert kernel, combine) on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "mega_moe.h"
+#include "moe_args.h"
+
+namespace mega_moe {
+void launch_dispatch(const MoeArgs& a, int gather_blocks, hipStream_t stream);
+int launch_expert_ffn(const MoeArgs& a, int num_cus, hipStream_t stream);
+void launch_combine(const MoeArgs& a, hipStream_t stream);
+}  // namespace mega_moe
+
+using namespace mega_moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return MEGA_MOE_OK;
+}
+
+int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Sizes that depend only on the configuration.
+struct Layout {
+    int64_t R_max, P_cap, PB_cap, chunks_max;
+    int64_t off[17];
+    int64_t total;
+};
+
+enum {
+    L_COUNTS, L_OFFSETS, L_MBSTART, L_PBEXP, L_SLOTMAP, L_SRC, L_CHIST, L_CBASE,
+    L_L1ACTS, L_L1SF, L_L1W, L_L2ACTS, L_L2SF, L_COMB, L_READY, L_CTRL, L_COUNT
+};
+
+int check_config(const mega_moe_config* c) {
+    if (!c) return fail(MEGA_MOE_ERR_INVALID_ARG, "config is NULL");
+    if (c->num_experts < 1 || c->num_experts > MAX_EXPERTS)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "num_experts must be in [1, %d], got %d", MAX_EXPERTS,
+                    c->num_experts);
+    if (c->hidden <= 0 || c->hidden % 128)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "hidden must be a positive multiple of 128, got %d",
+                    c->hidden);
+    if (c->intermediate <= 0 || c->intermediate % 128)
+        return fail(MEGA_MOE_ERR_INVALID_ARG,
+                    "intermediate must be a positive multiple of 128, got %d", c->intermediate);
+    if (c->num_topk < 1) return fail(MEGA_MOE_ERR_INVALID_ARG, "num_topk must be >= 1");
+    if (c->max_tokens < 0) return fail(MEGA_MOE_ERR_INVALID_ARG, "max_tokens must be >= 0");
+    if ((int64_t)c->max_tokens * c->num_topk > (int64_t)1 << 30)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "max_tokens * num_topk too large");
+    if (!(std::isinf(c->activation_clamp) && c->activation_clamp > 0))
+        return fail(MEGA_MOE_ERR_UNSUPPORTED, "only activation_clamp = +inf (no clamp) is built");
+    if (c->fast_math != 0) return fail(MEGA_MOE_ERR_UNSUPPORTED, "only fast_math = 0 is built");
+    if (c->block_m != 0 && c->block_m != 32 && c->block_m != 64 && c->block_m != 128)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "block_m must be 0, 32, 64 or 128");
+    if (c->l2_n_major < -1 || c->l2_n_major > 1)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "l2_n_major must be -1, 0 or 1");
+    return MEGA_MOE_OK;
+}
+
+Layout make_layout(const mega_moe_config& c) {
+    Layout L{};
+    const int64_t E = c.num_experts, H = c.hidden, I = c.intermediate;
+    L.R_max = (int64_t)c.max_tokens * c.num_topk;
+    // sum over experts of align_up(count, 128) <= R + 127 E
+    L.P_cap = align_up(L.R_max + (POOL_ALIGN - 1) * E, POOL_ALIGN);
+    L.PB_cap = L.P_cap / 32;           // pool blocks at the smallest BLOCK_M
+    L.chunks_max = (L.R_max + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK;
+    if (L.chunks_max < 1) L.chunks_max = 1;
+    int64_t sz[L_COUNT];
+    sz[L_COUNTS] = E * 4;
+    sz[L_OFFSETS] = (E + 1) * 4;
+    sz[L_MBSTART] = (E + 1) * 4;
+    sz[L_PBEXP] = L.PB_cap * 4;
+    sz[L_SLOTMAP] = L.R_max * 4;
+    sz[L_SRC] = L.P_cap * 4;
+    sz[L_CHIST] = L.chunks_max * E * 4;
+    sz[L_CBASE] = L.chunks_max * E * 4;
+    sz[L_L1ACTS] = L.P_cap * H;
+    sz[L_L1SF] = (H / 128) * L.P_cap * 4;
+    sz[L_L1W] = L.P_cap * 4;
+    sz[L_L2ACTS] = L.P_cap * I;
+    sz[L_L2SF] = (I / 64) * L.P_cap * 4;
+    sz[L_COMB] = L.R_max * H * 2;
+    sz[L_READY] = L.PB_cap * 4;
+    sz[L_CTRL] = sizeof(MoeCtrl);
+    int64_t o = 0;
+    for (int i = 0; i < L_COUNT; ++i) {
+        L.off[i] = o;
+        o = align_up(o + sz[i], 256);
+    }
+    L.total = o;
+    return L;
+}
+
+void plan(const mega_moe_config& c, int32_t T, mega_moe_plan_info* p) {
+    // expected routes per expert on one GPU (SM90 design 13.1 with one rank)
+    const float expected = float(T) * float(c.num_topk) / float(c.num_experts);
+    int bm;
+    if (c.block_m) bm = c.block_m;
+    else if (expected <= 16.5f) bm = 32;
+    else if (expected <= 64.5f) bm = 64;
+    else bm = 128;
+    int nm = c.l2_n_major;
+    if (nm < 0) nm = expected >= 256.0f ? 1 : 0;   // SM90 design 12.2
+    p->expected_tokens_per_expert = expected;
+    p->block_m = bm;
+    p->l2_n_major = nm;
+    p->l1_n_blocks = 2 * c.intermediate / 128;
+    p->l2_n_blocks = c.hidden / 128;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+struct mega_moe_handle {
+    mega_moe_config cfg;
+    Layout L;
+    int device;
+    int num_cus;
+    uint8_t* ws;
+    int32_t last_T;
+    MoeArgs base;   // workspace pointers and sizes filled at create
+    // optional event timing of the kernel groups (4 events per call)
+    std::vector<hipEvent_t> prof_events;
+    int32_t prof_max = 0, prof_used = 0;
+};
+
+namespace {
+void prof_release(mega_moe_handle* h) {
+    for (hipEvent_t ev : h->prof_events) hipEventDestroy(ev);
+    h->prof_events.clear();
+    h->prof_max = h->prof_used = 0;
+}
+
+hipEvent_t prof_event(mega_moe_handle* h, int call, int which) {
+    if (call < 0) return nullptr;
+    return h->prof_events[(size_t)call * 4 + which];
+}
+}  // namespace
+
+extern "C" {
+
+const char* mega_moe_last_error(void) { return g_last_error.c_str(); }
+
+int32_t mega_moe_token_alignment(void) { return POOL_ALIGN; }
+
+int64_t mega_moe_workspace_bytes(const mega_moe_config* cfg) {
+    if (check_config(cfg) != MEGA_MOE_OK) return -1;
+    return make_layout(*cfg).total;
+}
+
+int mega_moe_plan(const mega_moe_config* cfg, int32_t num_tokens, mega_moe_plan_info* out) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (!out) return fail(MEGA_MOE_ERR_INVALID_ARG, "out is NULL");
+    if (num_tokens < 0) return fail(MEGA_MOE_ERR_INVALID_ARG, "num_tokens < 0");
+    plan(*cfg, num_tokens, out);
+    return ok();
+}
+
+int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out) {
+    if (!out) return fail(MEGA_MOE_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MEGA_MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+        return fail(MEGA_MOE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(MEGA_MOE_ERR_UNSUPPORTED, "device %d is %s, this library is built for gfx950",
+                    dev, prop.gcnArchName);
+    auto* h = new mega_moe_handle{};
+    h->cfg = *cfg;
+    h->L = make_layout(*cfg);
+    h->device = dev;
+    h->num_cus = prop.multiProcessorCount;
+    e = hipMalloc((void**)&h->ws, h->L.total);
+    if (e != hipSuccess) {
+        const long long bytes = (long long)h->L.total;
+        delete h;
+        return fail(MEGA_MOE_ERR_OUT_OF_MEMORY, "hipMalloc(%lld): %s", bytes, hipGetErrorString(e));
+    }
+    e = hipMemset(h->ws, 0, h->L.total);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        hipFree(h->ws);
+        delete h;
+        return fail(MEGA_MOE_ERR_HIP, "workspace clear: %s", hipGetErrorString(e));
+    }
+    MoeArgs& a = h->base;
+    std::memset(&a, 0, sizeof a);
+    const Layout& L = h->L;
+    a.H = cfg->hidden;
+    a.I = cfg->intermediate;
+    a.E = cfg->num_experts;
+    a.k = cfg->num_topk;
+    a.P_cap = L.P_cap;
+    a.nb1 = 2 * cfg->intermediate / 128;
+    a.nb2 = cfg->hidden / 128;
+    a.wait_spin_limit = 1u << 22;
+    uint8_t* w = h->ws;
+    a.counts = (int32_t*)(w + L.off[L_COUNTS]);
+    a.offsets = (int32_t*)(w + L.off[L_OFFSETS]);
+    a.mb_start = (int32_t*)(w + L.off[L_MBSTART]);
+    a.pb_expert = (int32_t*)(w + L.off[L_PBEXP]);
+    a.slot_map = (int32_t*)(w + L.off[L_SLOTMAP]);
+    a.src = (int32_t*)(w + L.off[L_SRC]);
+    a.chunk_hist = (int32_t*)(w + L.off[L_CHIST]);
+    a.chunk_base = (int32_t*)(w + L.off[L_CBASE]);
+    a.l1_acts = w + L.off[L_L1ACTS];
+    a.l1_sf = (float*)(w + L.off[L_L1SF]);
+    a.l1_w = (float*)(w + L.off[L_L1W]);
+    a.l2_acts = w + L.off[L_L2ACTS];
+    a.l2_sf = (float*)(w + L.off[L_L2SF]);
+    a.comb = (uint16_t*)(w + L.off[L_COMB]);
+    a.ready = (uint32_t*)(w + L.off[L_READY]);
+    a.ctrl = (MoeCtrl*)(w + L.off[L_CTRL]);
+    h->last_T = 0;
+    *out = h;
+    return ok();
+}
+
+int mega_moe_destroy(mega_moe_handle* h) {
+    if (!h) return ok();
+    prof_release(h);
+    hipError_t e = hipFree(h->ws);
+    delete h;
+    if (e != hipSuccess) return fail(MEGA_MOE_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int mega_moe_forward(mega_moe_handle* h, int32_t T, const uint8_t* x, const float* x_sf,
+                     const int32_t* topk_idx, const float* topk_weights, const uint8_t* w1,
+                     const float* w1_sf, const uint8_t* w2, const float* w2_sf, uint16_t* y,
+                     void* stream_v) {
+    if (!h) return fail(MEGA_MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (T < 0 || T > h->cfg.max_tokens)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "num_tokens %d outside [0, max_tokens=%d]", T,
+                    h->cfg.max_tokens);
+    h->last_T = T;
+    if (T == 0) return ok();
+    if (!x || !x_sf || !topk_idx || !topk_weights || !w1 || !w1_sf || !w2 || !w2_sf || !y)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "a tensor pointer is NULL");
+    if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(y, 16))
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "x, w1, w2 and y must be 16-byte aligned");
+    if (!aligned(x_sf, 4) || !aligned(topk_idx, 4) || !aligned(topk_weights, 4) ||
+        !aligned(w1_sf, 4) || !aligned(w2_sf, 4))
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "scale, index and weight arrays must be 4-byte aligned");
+    hipStream_t stream = (hipStream_t)stream_v;
+    mega_moe_plan_info p;
+    plan(h->cfg, T, &p);
+    MoeArgs a = h->base;
+    a.T = T;
+    a.R = T * h->cfg.num_topk;
+    a.block_m = p.block_m;
+    a.n_major = p.l2_n_major;
+    a.num_chunks = (a.R + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK;
+    a.x = x;
+    a.x_sf = x_sf;
+    a.topk_idx = topk_idx;
+    a.topk_w = topk_weights;
+    a.w1 = w1;
+    a.w1_sf = w1_sf;
+    a.w2 = w2;
+    a.w2_sf = w2_sf;
+    a.y = y;
+    const int gather_blocks = a.R < 16384 ? a.R : 16384;
+    const int call = h->prof_used < h->prof_max ? h->prof_used++ : -1;
+    if (call >= 0) hipEventRecord(prof_event(h, call, 0), stream);
+    launch_dispatch(a, gather_blocks, stream);
+    if (call >= 0) hipEventRecord(prof_event(h, call, 1), stream);
+    launch_expert_ffn(a, h->num_cus, stream);
+    if (call >= 0) hipEventRecord(prof_event(h, call, 2), stream);
+    launch_combine(a, stream);
+    if (call >= 0) hipEventRecord(prof_event(h, call, 3), stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MEGA_MOE_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int mega_moe_get_status(mega_moe_handle* h, void* stream_v) {
+    if (!h) return fail(MEGA_MOE_ERR_INVALID_ARG, "handle is NULL");
+    hipStream_t stream = (hipStream_t)stream_v;
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(MEGA_MOE_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+    uint32_t bits = 0;
+    uint32_t* dev_err = &h->base.ctrl->error;
+    e = hipMemcpy(&bits, dev_err, sizeof bits, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && bits) e = hipMemset(dev_err, 0, sizeof bits);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail(MEGA_MOE_ERR_HIP, "status read: %s", hipGetErrorString(e));
+    ok();
+    return (int)bits;
+}
+
+int mega_moe_profile_begin(mega_moe_handle* h, int32_t max_calls) {
+    if (!h) return fail(MEGA_MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (max_calls < 1 || max_calls > 4096)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "max_calls must be in [1, 4096]");
+    prof_release(h);
+    h->prof_events.resize((size_t)max_calls * 4, nullptr);
+    for (auto& ev : h->prof_events) {
+        hipError_t e = hipEventCreate(&ev);
+        if (e != hipSuccess) {
+            ev = nullptr;
+            prof_release(h);
+            return fail(MEGA_MOE_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+        }
+    }
+    h->prof_max = max_calls;
+    h->prof_used = 0;
+    return ok();
+}
+
+int mega_moe_profile_end(mega_moe_handle* h, float* ms_out, int32_t capacity, int32_t* n_out) {
+    if (!h || !n_out || (capacity > 0 && !ms_out))
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "NULL argument");
+    const int n = h->prof_used < capacity ? h->prof_used : capacity;
+    for (int c = 0; c < n; ++c) {
+        hipError_t e = hipEventSynchronize(prof_event(h, c, 3));
+        for (int k = 0; k < 3 && e == hipSuccess; ++k)
+            e = hipEventElapsedTime(&ms_out[c * 3 + k], prof_event(h, c, k), prof_event(h, c, k + 1));
+        if (e != hipSuccess) {
+            prof_release(h);
+            return fail(MEGA_MOE_ERR_HIP, "event timing: %s", hipGetErrorString(e));
+        }
+    }
+    *n_out = n;
+    prof_release(h);
+    return ok();
+}
+
+int mega_moe_get_views(mega_moe_handle* h, mega_moe_views* v) {
+    if (!h || !v) return fail(MEGA_MOE_ERR_INVALID_ARG, "NULL argument");
+    const MoeArgs& a = h->base;
+    v->counts = a.counts;
+    v->offsets = a.offsets;
+    v->slot_map = a.slot_map;
+    v->src = a.src;
+    v->l1_acts = a.l1_acts;
+    v->l1_acts_sf = a.l1_sf;
+    v->l1_topk_weights = a.l1_w;
+    v->l2_acts = a.l2_acts;
+    v->l2_acts_sf = a.l2_sf;
+    v->combine_buf = a.comb;
+    v->pool_rows_capacity = a.P_cap;
+    v->last_num_tokens = h->last_T;
+    return ok();
+}
+
+}  // extern "C"

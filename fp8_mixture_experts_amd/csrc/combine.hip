@@ -1,0 +1,63 @@
+// Top-k combine: y[t, n] = bf16( sum over active slots j, ascending, of
+// float32(partial[t*k + j, n]) ), a float32 running sum from +0 ("MegaMoE SM90
+// Implementation Design (Final)" 11.2; "PR357 Green-Context Split MegaMoE
+// code review" 6.3).  A slot is active when 0 <= topk_idx < E.
+//
+// HBM-bound: each thread owns 8 consecutive columns (16-byte loads and
+// stores) of one token and walks its k partial rows in slot order; a row of
+// H columns is covered by H/8 threads, so every load instruction of a wave
+// reads 1 KB of one contiguous partial row.
+#include <hip/hip_runtime.h>
+
+#include "moe_args.h"
+
+namespace mega_moe {
+
+constexpr int COMBINE_THREADS = 128;
+constexpr int COMBINE_COLS = COMBINE_THREADS * 8;   // columns per workgroup
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    auto rne = [](float f) -> uint32_t {
+        uint32_t u = __float_as_uint(f);
+        if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+        u += 0x7fffu + ((u >> 16) & 1u);
+        return u >> 16;
+    };
+    return rne(lo) | (rne(hi) << 16);
+}
+
+__global__ void __launch_bounds__(COMBINE_THREADS)
+moe_combine(MoeArgs a) {
+    const int col_blocks = (a.H + COMBINE_COLS - 1) / COMBINE_COLS;
+    const int t = blockIdx.x / col_blocks;
+    const int col = (blockIdx.x - t * col_blocks) * COMBINE_COLS + threadIdx.x * 8;
+    if (col >= a.H) return;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < a.k; ++j) {
+        const int e = a.topk_idx[(size_t)t * a.k + j];
+        if (e < 0 || e >= a.E) continue;
+        const uint4 p = *reinterpret_cast<const uint4*>(a.comb + ((size_t)t * a.k + j) * a.H + col);
+        const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += __uint_as_float(w[i] << 16);
+            acc[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    uint4 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>(a.y + (size_t)t * a.H + col) = o;
+}
+
+void launch_combine(const MoeArgs& a, hipStream_t stream) {
+    const int col_blocks = (a.H + COMBINE_COLS - 1) / COMBINE_COLS;
+    dim3 grid(col_blocks * a.T);
+    hipLaunchKernelGGL(moe_combine, grid, dim3(COMBINE_THREADS), 0, stream, a);
+}
+
+}  // namespace mega_moe

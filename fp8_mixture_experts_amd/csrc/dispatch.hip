@@ -1,0 +1,229 @@
+// Dispatch of the expert layer: per-expert histogram, prefix scan into
+// 128-aligned pool segments, a stable slot for every route and the copy of
+// each routed token into its expert's pool ("MegaMoE SM90 Implementation
+// Design (Final)" 3.3 phase 1 and 9.2; one GPU, so every source is local).
+//
+// Four launches, all on the caller's stream:
+//   moe_dispatch_count   one workgroup per chunk of 1024 routes: histogram
+//   moe_dispatch_scan    one workgroup: per-expert scan over chunks, the
+//                        wavefront prefix scan over experts (offsets, pool
+//                        blocks), padding metadata, reset of the expert
+//                        kernel's queue and arrival counters
+//   moe_dispatch_scatter one workgroup per chunk: stable rank of every route
+//                        inside its expert (wave ballots), slot map and source
+//                        metadata
+//   moe_dispatch_gather  copy of the FP8 row, its scales and its top-k weight
+//                        into the pool row of every route
+#include <hip/hip_runtime.h>
+
+#include "moe_args.h"
+#include "mega_moe.h"
+
+namespace mega_moe {
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__global__ void __launch_bounds__(DISPATCH_THREADS)
+moe_dispatch_count(MoeArgs a) {
+    __shared__ int hist[MAX_EXPERTS];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < a.E; e += DISPATCH_THREADS) hist[e] = 0;
+    __syncthreads();
+    const int f0 = blockIdx.x * DISPATCH_CHUNK;
+    bool bad = false;
+    for (int i = tid; i < DISPATCH_CHUNK; i += DISPATCH_THREADS) {
+        const int f = f0 + i;
+        if (f < a.R) {
+            const int e = a.topk_idx[f];
+            if (e >= 0 && e < a.E) atomicAdd(&hist[e], 1);
+            else if (e >= a.E) bad = true;
+        }
+    }
+    if (bad) atomicOr(&a.ctrl->error, MEGA_MOE_DEVERR_BAD_EXPERT);
+    __syncthreads();
+    for (int e = tid; e < a.E; e += DISPATCH_THREADS)
+        a.chunk_hist[(size_t)blockIdx.x * a.E + e] = hist[e];
+}
+
+// Exclusive scan of one int per thread over a workgroup of SCAN_THREADS
+// (wave64 inclusive scan by shuffles, then a scan of the wave totals).
+constexpr int SCAN_THREADS = 1024;
+
+__device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
+    const int lane = lane_id();
+    const int wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int n = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += n;
+    }
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        const int nw = SCAN_THREADS / 64;
+        int w = lane < nw ? s_wave[lane] : 0;
+        int wi = w;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int n = __shfl_up(wi, d, 64);
+            if (lane >= d) wi += n;
+        }
+        if (lane < nw) s_wave[lane] = wi - w;       // exclusive prefix of wave totals
+        if (lane == nw - 1) s_wave[SCAN_THREADS / 64] = wi;
+    }
+    __syncthreads();
+    const int out = s_wave[wave] + incl - v;
+    *total = s_wave[SCAN_THREADS / 64];
+    __syncthreads();
+    return out;
+}
+
+__global__ void __launch_bounds__(SCAN_THREADS)
+moe_dispatch_scan(MoeArgs a) {
+    __shared__ int s_count[MAX_EXPERTS];
+    __shared__ int s_off[MAX_EXPERTS + 1];
+    __shared__ int s_mb[MAX_EXPERTS + 1];
+    __shared__ int s_wave[SCAN_THREADS / 64 + 1];
+    const int tid = threadIdx.x;
+    const int E = a.E;
+
+    // per expert: running sum over chunks (relative chunk bases) and count
+    for (int e = tid; e < E; e += SCAN_THREADS) {
+        int run = 0;
+        for (int c = 0; c < a.num_chunks; ++c) {
+            const size_t i = (size_t)c * E + e;
+            const int h = a.chunk_hist[i];
+            a.chunk_base[i] = run;
+            run += h;
+        }
+        s_count[e] = run;
+        a.counts[e] = run;
+    }
+    __syncthreads();
+
+    // prefix scan over experts (E <= SCAN_THREADS): padded segments, pool blocks
+    const int e = tid;
+    const int cnt = e < E ? s_count[e] : 0;
+    const int padded = (cnt + POOL_ALIGN - 1) / POOL_ALIGN * POOL_ALIGN;
+    const int mbs = (cnt + a.block_m - 1) / a.block_m;
+    int total_rows = 0, total_mb = 0;
+    const int off = block_exclusive_scan(padded, s_wave, &total_rows);
+    const int mb0 = block_exclusive_scan(mbs, s_wave, &total_mb);
+    if (e < E) {
+        s_off[e] = off;
+        s_mb[e] = mb0;
+        a.offsets[e] = off;
+        a.mb_start[e] = mb0;
+    }
+    if (tid == 0) {
+        s_off[E] = total_rows;
+        s_mb[E] = total_mb;
+        a.offsets[E] = total_rows;
+        a.mb_start[E] = total_mb;
+        a.ctrl->total_mb = total_mb;
+        a.ctrl->next_tile = 0;
+    }
+    __syncthreads();
+
+    // absolute chunk bases
+    const size_t ce = (size_t)a.num_chunks * E;
+    for (size_t i = tid; i < ce; i += SCAN_THREADS) a.chunk_base[i] += s_off[i % E];
+
+    // padding rows of every segment hold no route
+    for (int ex = 0; ex < E; ++ex) {
+        const int pad0 = s_off[ex] + s_count[ex];
+        const int pad1 = s_off[ex + 1];
+        for (int r = pad0 + tid; r < pad1; r += SCAN_THREADS) a.src[r] = -1;
+    }
+
+    // expert of every pool block, and a cleared arrival counter for it
+    for (int pb = tid; pb < total_mb; pb += SCAN_THREADS) {
+        int lo = 0, hi = E - 1;               // last expert with s_mb[ex] <= pb
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_mb[mid] <= pb) lo = mid; else hi = mid - 1;
+        }
+        a.pb_expert[pb] = lo;
+        a.ready[pb] = 0;
+    }
+}
+
+__global__ void __launch_bounds__(DISPATCH_THREADS)
+moe_dispatch_scatter(MoeArgs a) {
+    constexpr int NW = DISPATCH_THREADS / 64;
+    __shared__ int running[MAX_EXPERTS];
+    __shared__ int wcnt[NW][MAX_EXPERTS];
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    const int E = a.E;
+    const int c = blockIdx.x;
+    int key_bits = 0;
+    while ((1 << key_bits) <= E) ++key_bits;   // keys 0..E (E = "no expert")
+
+    for (int e = tid; e < E; e += DISPATCH_THREADS) running[e] = 0;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    for (int round = 0; round < DISPATCH_CHUNK / DISPATCH_THREADS; ++round) {
+        for (int i = tid; i < NW * E; i += DISPATCH_THREADS) wcnt[i / E][i % E] = 0;
+        __syncthreads();
+        const int f = c * DISPATCH_CHUNK + round * DISPATCH_THREADS + tid;
+        int e = f < a.R ? a.topk_idx[f] : -1;
+        const bool valid = e >= 0 && e < E;
+        const int key = valid ? e : E;
+        // lanes of this wave with the same key (a match by ballots, bit by bit)
+        uint64_t peers = __ballot(1);
+        for (int b = 0; b < key_bits; ++b) {
+            const bool bit = (key >> b) & 1;
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        const int rank = __popcll(peers & lt_mask);
+        if (valid && rank == 0) wcnt[wave][e] = __popcll(peers);
+        __syncthreads();
+        if (valid) {
+            int before = running[e] + rank;
+            for (int w = 0; w < wave; ++w) before += wcnt[w][e];
+            const int slot = a.chunk_base[(size_t)c * E + e] + before;
+            a.slot_map[f] = slot;
+            a.src[slot] = f;
+        } else if (f < a.R) {
+            a.slot_map[f] = -1;
+        }
+        __syncthreads();
+        for (int ex = tid; ex < E; ex += DISPATCH_THREADS) {
+            int s = 0;
+            for (int w = 0; w < NW; ++w) s += wcnt[w][ex];
+            running[ex] += s;
+        }
+        __syncthreads();
+    }
+}
+
+__global__ void __launch_bounds__(256)
+moe_dispatch_gather(MoeArgs a) {
+    const int tid = threadIdx.x;
+    const int H = a.H;
+    const int kb_n = H / 128;
+    for (int f = blockIdx.x; f < a.R; f += gridDim.x) {
+        const int slot = a.slot_map[f];
+        if (slot < 0) continue;
+        const int t = f / a.k;
+        const uint4* s = reinterpret_cast<const uint4*>(a.x + (size_t)t * H);
+        uint4* d = reinterpret_cast<uint4*>(a.l1_acts + (size_t)slot * H);
+        for (int i = tid; i < H / 16; i += blockDim.x) d[i] = s[i];
+        for (int i = tid; i < kb_n; i += blockDim.x)
+            a.l1_sf[(size_t)i * a.P_cap + slot] = a.x_sf[(size_t)t * kb_n + i];
+        if (tid == 0) a.l1_w[slot] = a.topk_w[f];
+    }
+}
+
+void launch_dispatch(const MoeArgs& a, int gather_blocks, hipStream_t stream) {
+    hipLaunchKernelGGL(moe_dispatch_count, dim3(a.num_chunks), dim3(DISPATCH_THREADS), 0, stream, a);
+    hipLaunchKernelGGL(moe_dispatch_scan, dim3(1), dim3(SCAN_THREADS), 0, stream, a);
+    hipLaunchKernelGGL(moe_dispatch_scatter, dim3(a.num_chunks), dim3(DISPATCH_THREADS), 0, stream, a);
+    hipLaunchKernelGGL(moe_dispatch_gather, dim3(gather_blocks), dim3(256), 0, stream, a);
+}
+
+}  // namespace mega_moe

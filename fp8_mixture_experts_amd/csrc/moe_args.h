@@ -1,0 +1,65 @@
+// Shared between the host code and the kernels: the argument block every
+// kernel of one forward call receives, and the small control record in the
+// workspace.
+#pragma once
+
+#include <stdint.h>
+
+namespace mega_moe {
+
+// Control record in device memory, reset by the dispatch scan of every call.
+struct MoeCtrl {
+    int32_t next_tile;   // work queue head of the persistent expert kernel
+    int32_t total_mb;    // number of pool blocks (BLOCK_M rows) over all experts
+    uint32_t error;      // sticky MEGA_MOE_DEVERR_* bits
+    int32_t done_blocks; // reserved
+};
+
+struct MoeArgs {
+    // shapes of this call
+    int32_t T, H, I, E, k;
+    int32_t R;          // T * k routes
+    int64_t P_cap;      // pool rows allocated (row stride of the pool-minor arrays)
+    int32_t block_m;    // rows per pool block for the expert kernel
+    int32_t nb1;        // L1 N blocks: 2I / 128
+    int32_t nb2;        // L2 N blocks: H / 128
+    int32_t n_major;    // L2 tile order: 1 = consecutive tiles share a W2 N block
+    int32_t num_chunks; // dispatch chunks of DISPATCH_CHUNK routes
+    uint32_t wait_spin_limit;  // bound on one L2 tile's wait for its L1 tiles
+
+    // inputs (caller-owned)
+    const uint8_t* x;
+    const float* x_sf;
+    const int32_t* topk_idx;
+    const float* topk_w;
+    const uint8_t* w1;
+    const float* w1_sf;
+    const uint8_t* w2;
+    const float* w2_sf;
+    uint16_t* y;
+
+    // workspace (handle-owned)
+    int32_t* counts;      // [E]
+    int32_t* offsets;     // [E+1]
+    int32_t* mb_start;    // [E+1] first pool block of each expert
+    int32_t* pb_expert;   // [PB_cap] expert of each pool block
+    int32_t* slot_map;    // [R]
+    int32_t* src;         // [P_cap]
+    int32_t* chunk_hist;  // [num_chunks, E]
+    int32_t* chunk_base;  // [num_chunks, E]
+    uint8_t* l1_acts;     // [P_cap, H]
+    float* l1_sf;         // [H/128, P_cap]
+    float* l1_w;          // [P_cap]
+    uint8_t* l2_acts;     // [P_cap, I]
+    float* l2_sf;         // [I/64, P_cap]
+    uint16_t* comb;       // [R, H]
+    uint32_t* ready;      // [PB_cap] finished L1 tiles per pool block
+    MoeCtrl* ctrl;
+};
+
+constexpr int DISPATCH_CHUNK = 1024;    // routes per dispatch workgroup
+constexpr int DISPATCH_THREADS = 256;
+constexpr int POOL_ALIGN = 128;         // pool segment alignment (largest BLOCK_M)
+constexpr int MAX_EXPERTS = 1024;
+
+}  // namespace mega_moe

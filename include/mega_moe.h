@@ -1,0 +1,185 @@
+/*
+ * mega_moe.h - C ABI of the fused FP8 mixture-of-experts expert layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the one the page "MegaMoE SM90 Implementation Design (Final)"
+ * describes (cited as "SM90 design" with its section numbers), run as one
+ * GPU's share of expert parallelism: all E experts are local and every routed
+ * token is local.  One forward call computes, on the caller's HIP stream:
+ *
+ *   1. dispatch       per-expert counts, 128-aligned pool offsets, a stable
+ *                     slot per (token, top-k slot) route, source metadata, and
+ *                     the permuted per-expert pool of FP8 rows, their float
+ *                     scales and top-k weights            (SM90 design 3.3, 9.2)
+ *   2. L1 GEMM        FP8 x FP8 with one float scale per 128 K for the
+ *                     activations (per token) and per 128x128 block for W1;
+ *                     W1 rows are gate/up interleaved by 8  (5.1-5.3, 15.1-15.2)
+ *   3. SwiGLU         silu(gate) * up * top-k weight            (10.1 steps 1-3)
+ *   4. re-quantise    per row and 64 columns: sf = amax / 448,
+ *                     code = e4m3(h / sf)                        (10.1 steps 4-6)
+ *   5. L2 GEMM        FP8 x FP8, each 128-K block split in two 64-K halves with
+ *                     their own activation scales; result cast to BF16 (5.4, 11.1)
+ *   6. combine        per token, FP32 sum of the BF16 partials of its active
+ *                     slots in slot order, cast to BF16        (11.2; "PR357
+ *                     Green-Context Split MegaMoE code review" 6.3)
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are owned by the caller, row-major and contiguous.
+ *     x, W1, W2 and y must be 16-byte aligned; float and int arrays 4-byte.
+ *   - FP8 is OCP E4M3 ("fn": no infinities, 0x7F/0xFF are NaN, max 448).
+ *     BF16 is passed as uint16_t bit patterns.
+ *   - Return value 0 (MEGA_MOE_OK) or a negative mega_moe_status; on error
+ *     mega_moe_last_error() gives a message for the calling thread.
+ *   - Streams are hipStream_t passed as void* (NULL = the null stream).
+ */
+#ifndef MEGA_MOE_H_
+#define MEGA_MOE_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mega_moe_status {
+    MEGA_MOE_OK = 0,
+    MEGA_MOE_ERR_INVALID_ARG = -1,   /* bad shape, null or misaligned pointer   */
+    MEGA_MOE_ERR_UNSUPPORTED = -2,   /* device is not gfx950, or option not built */
+    MEGA_MOE_ERR_HIP = -3,           /* a HIP runtime call failed               */
+    MEGA_MOE_ERR_OUT_OF_MEMORY = -4, /* workspace allocation failed             */
+    MEGA_MOE_ERR_DEVICE = -5         /* the device flagged an error (see get_status) */
+} mega_moe_status;
+
+/* Device error bits reported by mega_moe_get_status (sticky until read). */
+#define MEGA_MOE_DEVERR_BAD_EXPERT 0x1u   /* a topk_idx >= num_experts (route skipped) */
+#define MEGA_MOE_DEVERR_WAIT_TIMEOUT 0x2u /* an L2 tile gave up waiting for its L1 tiles */
+
+/*
+ * Layer configuration (SM90 design 16.1: the expert count, top-k, the
+ * per-rank token bound and the activation options are fixed per layer).
+ */
+typedef struct mega_moe_config {
+    int32_t num_experts;      /* E, local experts, >= 1                          */
+    int32_t hidden;           /* H, multiple of 128                              */
+    int32_t intermediate;     /* I, multiple of 128 (W1 has 2*I rows)            */
+    int32_t num_topk;         /* k, 1 <= k                                        */
+    int32_t max_tokens;       /* largest T a forward call may pass, >= 0          */
+    float activation_clamp;   /* clamp of gate/up before SwiGLU (SM90 design 10.1
+                                 step 3); only +inf (no clamp) is supported       */
+    int32_t fast_math;        /* 0: accurate exp and division in SwiGLU (only 0) */
+    int32_t block_m;          /* 0 = automatic (SM90 design 13.1), else 32/64/128 */
+    int32_t l2_n_major;       /* -1 automatic (12.2), 0 M-major, 1 N-major L2 order */
+} mega_moe_config;
+
+typedef struct mega_moe_handle mega_moe_handle;
+
+/*
+ * Validates cfg (H % 128 == 0, I % 128 == 0, k >= 1, E >= 1, unsupported
+ * options rejected) on the current HIP device, checks that it is gfx950, and
+ * allocates the handle-owned workspace for max_tokens (pool, re-quantised
+ * activations, BF16 partials, counters, metadata).  *out is set to NULL on error.
+ */
+int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out);
+
+/*
+ * One forward pass of the layer, asynchronous on `stream` (no host
+ * synchronisation, no allocation).  Shapes (T = num_tokens):
+ *   x            [T, H]            uint8 E4M3 activations
+ *   x_sf         [T, H/128]        float scale per token per 128 channels
+ *   topk_idx     [T, k]            int32 expert of each slot; < 0 = inactive
+ *                                  slot; >= E sets MEGA_MOE_DEVERR_BAD_EXPERT
+ *                                  and the slot is treated as inactive
+ *   topk_weights [T, k]            float
+ *   w1           [E, 2I, H]        uint8 E4M3, rows gate/up interleaved by 8:
+ *                                  row 16g+r (r < 8) is the gate row of output
+ *                                  8g+r, row 16g+8+r its up row (SM90 design 15.1)
+ *   w1_sf        [E, 2I/128, H/128] float, one per 128x128 block of w1 as stored
+ *   w2           [E, H, I]         uint8 E4M3
+ *   w2_sf        [E, H/128, I/128] float
+ *   y            [T, H]            uint16 BF16 output; rows of tokens with no
+ *                                  active slot are +0
+ * num_tokens == 0 is a valid no-op; num_tokens > max_tokens is INVALID_ARG.
+ * One handle must not run on two streams at once (the workspace is shared);
+ * every call resets the workspace state it uses, so calls may follow each
+ * other freely on one stream.
+ */
+int mega_moe_forward(mega_moe_handle* h, int32_t num_tokens,
+                     const uint8_t* x, const float* x_sf,
+                     const int32_t* topk_idx, const float* topk_weights,
+                     const uint8_t* w1, const float* w1_sf,
+                     const uint8_t* w2, const float* w2_sf,
+                     uint16_t* y, void* stream);
+
+/* Frees the workspace and the handle; NULL is accepted. */
+int mega_moe_destroy(mega_moe_handle* h);
+
+/*
+ * Synchronises `stream`, then returns (and clears) the sticky device error
+ * bits (MEGA_MOE_DEVERR_*) as a non-negative value, or a negative status.
+ */
+int mega_moe_get_status(mega_moe_handle* h, void* stream);
+
+/* Message for the last non-zero return on the calling thread ("" if none). */
+const char* mega_moe_last_error(void);
+
+/* Workspace bytes mega_moe_create would allocate for cfg (-1 if invalid).
+ * Host-only; needs no GPU. */
+int64_t mega_moe_workspace_bytes(const mega_moe_config* cfg);
+
+/* Row alignment of every expert's pool segment (= the largest BLOCK_M, 128;
+ * SM90 design 13.1).  Host-only. */
+int32_t mega_moe_token_alignment(void);
+
+/*
+ * Host plan of one call (SM90 design 12.2 and 13.1): expected routes per
+ * expert T*k/E, BLOCK_M (<= 16.5 -> 32, <= 64.5 -> 64, else 128, unless
+ * cfg->block_m forces one) and whether the L2 tiles run N-major (expected >=
+ * 256, unless forced).  Host-only; needs no GPU.
+ */
+typedef struct mega_moe_plan_info {
+    float expected_tokens_per_expert;
+    int32_t block_m;
+    int32_t l2_n_major;
+    int32_t l1_n_blocks;      /* 2I / 128 */
+    int32_t l2_n_blocks;      /* H / 128  */
+} mega_moe_plan_info;
+int mega_moe_plan(const mega_moe_config* cfg, int32_t num_tokens, mega_moe_plan_info* out);
+
+/*
+ * Device views of the intermediates of the last forward call (the buffer views
+ * of SM90 design 16.1 / "PR357 review" 3.1), valid once its stream has
+ * synchronised and until the next call.  P = pool_rows_capacity.
+ */
+typedef struct mega_moe_views {
+    int32_t* counts;        /* [E]     routes per expert                         */
+    int32_t* offsets;       /* [E+1]   pool segment starts, 128-aligned          */
+    int32_t* slot_map;      /* [T*k]   pool row of route t*k+j, -1 if inactive   */
+    int32_t* src;           /* [P]     route t*k+j held by a pool row, -1 = pad  */
+    uint8_t* l1_acts;       /* [P, H]  pool of FP8 rows                          */
+    float* l1_acts_sf;      /* [H/128, P] their scales (pool-row minor)          */
+    float* l1_topk_weights; /* [P]     their top-k weights                       */
+    uint8_t* l2_acts;       /* [P, I]  re-quantised SwiGLU output                */
+    float* l2_acts_sf;      /* [I/64, P] its per-64 scales (pool-row minor)      */
+    uint16_t* combine_buf;  /* [T*k, H] BF16 L2 partial of each active route     */
+    int64_t pool_rows_capacity;
+    int32_t last_num_tokens;
+} mega_moe_views;
+int mega_moe_get_views(mega_moe_handle* h, mega_moe_views* out);
+
+/*
+ * Optional timing of the three kernel groups of the next forward calls with
+ * HIP events recorded on each call's stream (for benchmarks; the layer
+ * computes the same thing with or without it).  profile_begin arms it for up
+ * to max_calls calls (1..4096); profile_end waits for those events and writes
+ * n_out rows of three float milliseconds per call (dispatch, expert kernel,
+ * combine) into ms_out[capacity][3], then disarms.  Calls beyond max_calls
+ * are not timed.
+ */
+int mega_moe_profile_begin(mega_moe_handle* h, int32_t max_calls);
+int mega_moe_profile_end(mega_moe_handle* h, float* ms_out, int32_t capacity, int32_t* n_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEGA_MOE_H_ */

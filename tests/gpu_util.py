@@ -1,0 +1,138 @@
+"""Helpers for the GPU parity tests: upload inputs, run the layer through the
+C ABI, read its intermediate views back, and the comparison rules.
+
+Acceptance rules (the benchmark spec's tolerances of this layer):
+* dispatch metadata (counts, offsets, slot map, source rows) and the pool
+  copies: bit-exact;
+* re-quantised activations over valid pool rows: at least 99.9% of the FP8
+  codes identical to the oracle's, the rest within one code step on the
+  ordered code line (+0 and -0 equal); their float scales within 1e-5
+  relative;
+* output y: relative Frobenius error at most 2e-3 (computed in float64).
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from fp8_mixture_experts_amd import binding as B
+from oracle import codecs
+
+_hip = None
+
+
+def _hip_rt():
+    global _hip
+    if _hip is None:
+        torch.cuda.init()
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        _hip.hipMemcpy.restype = ctypes.c_int
+    return _hip
+
+
+def d2h(ptr: int, shape, dtype) -> np.ndarray:
+    out = np.empty(shape, dtype=dtype)
+    if out.nbytes:
+        rc = _hip_rt().hipMemcpy(out.ctypes.data, ptr, out.nbytes, 2)  # device -> host
+        assert rc == 0, f"hipMemcpy failed: {rc}"
+    return out
+
+
+def to_device(inp, dev="cuda:0"):
+    t = {}
+    for key in ("x", "x_sf", "topk_idx", "topk_weights", "w1", "w1_sf", "w2", "w2_sf"):
+        t[key] = torch.from_numpy(np.ascontiguousarray(inp[key])).to(dev)
+    T, H = inp["x"].shape
+    t["y"] = torch.empty((T, H), dtype=torch.int16, device=dev)
+    return t
+
+
+class Runner:
+    """One layer handle sized for a workload; runs forwards and reads views."""
+
+    def __init__(self, inp, max_tokens=None, **cfg):
+        E, N, H = inp["w1"].shape
+        k = inp["topk_idx"].shape[1]
+        T = inp["x"].shape[0]
+        self.E, self.H, self.I, self.k = E, H, N // 2, k
+        self.layer = B.MegaMoE(E, H, N // 2, k, max_tokens if max_tokens is not None else T, **cfg)
+        self.dev = to_device(inp)
+
+    def forward(self, dev=None, num_tokens=None):
+        d = dev or self.dev
+        T = d["x"].shape[0] if num_tokens is None else num_tokens
+        stream = torch.cuda.current_stream().cuda_stream
+        B.mega_moe_forward(self.layer.handle, T, d["x"], d["x_sf"], d["topk_idx"],
+                           d["topk_weights"], d["w1"], d["w1_sf"], d["w2"], d["w2_sf"], d["y"],
+                           stream)
+        status = self.layer.status()
+        return status
+
+    def y(self, dev=None):
+        d = dev or self.dev
+        return d["y"].cpu().numpy().view(np.uint16)
+
+    def views(self, T, full=True):
+        v = self.layer.views()
+        E, H, I, k = self.E, self.H, self.I, self.k
+        Pc = v.pool_rows_capacity
+        out = dict(counts=d2h(v.counts, (E,), np.int32), offsets=d2h(v.offsets, (E + 1,), np.int32),
+                   slot_map=d2h(v.slot_map, (T, k), np.int32))
+        P = int(out["offsets"][-1])
+        out["P"] = P
+        out["src"] = d2h(v.src, (P,), np.int32)
+        out["l1_w"] = d2h(v.l1_topk_weights, (P,), np.float32)
+        out["l1_sf"] = d2h(v.l1_acts_sf, (H // 128, Pc), np.float32)[:, :P]
+        out["l2_sf"] = d2h(v.l2_acts_sf, (I // 64, Pc), np.float32)[:, :P]
+        out["l2_acts"] = d2h(v.l2_acts, (P, I), np.uint8)
+        if full:
+            out["l1_acts"] = d2h(v.l1_acts, (P, H), np.uint8)
+            out["comb"] = d2h(v.combine_buf, (T * k, H), np.uint16)
+        return out
+
+    def close(self):
+        self.layer.close()
+
+
+def ordered_codes(c):
+    c = np.asarray(c).astype(np.int32)
+    return np.where(c & 0x80, -(c & 0x7F), c)
+
+
+def check_codes(got, want, label=""):
+    """>= 99.9% identical E4M3 codes, the rest within one code step."""
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape
+    if got.size == 0:
+        return 1.0
+    diff = np.abs(ordered_codes(got) - ordered_codes(want))
+    same = float(np.mean(diff == 0))
+    assert diff.max() <= 1, f"{label}: code off by {diff.max()} steps"
+    assert same >= 0.999, f"{label}: only {same:.5f} of codes identical"
+    return same
+
+
+def check_sf(got, want, label="", rtol=1e-5):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    err = np.abs(got - want) / np.maximum(np.abs(want), 1e-30)
+    assert err.max() <= rtol, f"{label}: scale rel err {err.max():.3g}"
+
+
+def rel_frobenius(got_bf16, want_bf16):
+    g = codecs.bf16_to_f32(got_bf16).astype(np.float64)
+    w = codecs.bf16_to_f32(want_bf16).astype(np.float64)
+    den = np.linalg.norm(w)
+    return float(np.linalg.norm(g - w) / den) if den > 0 else float(np.linalg.norm(g))
+
+
+def check_y(got, want, label="", tol=2e-3):
+    assert np.all(np.isfinite(codecs.bf16_to_f32(got))), f"{label}: non-finite y"
+    r = rel_frobenius(got, want)
+    assert r <= tol, f"{label}: y relative Frobenius error {r:.3g} > {tol}"
+    return r

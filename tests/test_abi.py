@@ -1,0 +1,110 @@
+"""C-ABI library checks that need no GPU: it loads, exports every entry point
+its header declares, validates configurations, and plans calls by the tiers of
+"MegaMoE SM90 Implementation Design (Final)" 12.2 and 13.1 (golden file)."""
+
+import math
+import os
+import re
+
+import pytest
+
+from fp8_mixture_experts_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def _declared():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", f)).read()
+            names |= set(re.findall(r"^\s*(?:int|int32_t|int64_t|const char\*)\s+(mega_moe_\w+)\s*\(",
+                                    txt, flags=re.M))
+    return names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"mega_moe_create", "mega_moe_forward", "mega_moe_destroy"} <= names
+    assert names == set(B.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_token_alignment_is_largest_block_m(lib):
+    assert B.mega_moe_token_alignment() == 128
+
+
+def _cfg(**kw):
+    base = dict(num_experts=32, hidden=7168, intermediate=2048, num_topk=8, max_tokens=128)
+    base.update(kw)
+    return B.make_config(**base)
+
+
+def test_plan_matches_golden_tiers():
+    rows = [l.split() for l in open(os.path.join(ROOT, "tests/golden/block_m_tiers.txt"))
+            if l.strip() and not l.startswith("#")]
+    assert len(rows) >= 10
+    for t, k, e, exp, bm, nm in rows:
+        cfg = _cfg(num_experts=int(e), num_topk=int(k), max_tokens=max(int(t), 1))
+        p = B.mega_moe_plan(cfg, int(t))
+        assert math.isclose(p.expected_tokens_per_expert, float(exp), rel_tol=1e-6)
+        assert (p.block_m, p.l2_n_major) == (int(bm), int(nm)), (t, k, e)
+        assert p.l1_n_blocks == 2 * 2048 // 128 and p.l2_n_blocks == 7168 // 128
+
+
+def test_plan_overrides():
+    p = B.mega_moe_plan(_cfg(block_m=32, l2_n_major=1), 8192)
+    assert p.block_m == 32 and p.l2_n_major == 1
+    p = B.mega_moe_plan(_cfg(block_m=128, l2_n_major=0), 1)
+    assert p.block_m == 128 and p.l2_n_major == 0
+
+
+@pytest.mark.parametrize("kw", [dict(hidden=100), dict(intermediate=192), dict(num_topk=0),
+                                dict(num_experts=0), dict(num_experts=5000), dict(max_tokens=-1),
+                                dict(block_m=48), dict(l2_n_major=2)])
+def test_invalid_configs_are_rejected(kw):
+    assert B.mega_moe_workspace_bytes(_cfg(**kw)) == -1
+    with pytest.raises(B.MegaMoEError) as ei:
+        B.mega_moe_plan(_cfg(**kw), 1)
+    assert ei.value.code == B.MEGA_MOE_ERR_INVALID_ARG
+    assert B.mega_moe_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(activation_clamp=10.0), dict(fast_math=1)])
+def test_unbuilt_options_are_unsupported(kw):
+    with pytest.raises(B.MegaMoEError) as ei:
+        B.mega_moe_plan(_cfg(**kw), 1)
+    assert ei.value.code == B.MEGA_MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_bytes_cover_the_layer_buffers():
+    cfg = _cfg(max_tokens=8192)
+    n = B.mega_moe_workspace_bytes(cfg)
+    R = 8192 * 8
+    P = R + 127 * 32
+    # pool + re-quantised acts + BF16 partials dominate
+    assert n >= P * 7168 + P * 2048 + R * 7168 * 2
+    assert n < 1.1 * (P * 7168 + P * 2048 + R * 7168 * 2) + (64 << 20)
+    assert B.mega_moe_workspace_bytes(_cfg(max_tokens=0)) > 0
+
+
+def test_forward_rejects_bad_calls_without_touching_the_gpu():
+    # NULL handle and out-of-range token counts fail synchronously
+    with pytest.raises(B.MegaMoEError) as ei:
+        B.mega_moe_forward(None, 4, *([0] * 9), None)
+    assert ei.value.code == B.MEGA_MOE_ERR_INVALID_ARG
+
+
+def test_create_without_gpu_fails_cleanly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(B.MegaMoEError) as ei:
+        B.mega_moe_create(_cfg())
+    assert ei.value.code in (B.MEGA_MOE_ERR_HIP, B.MEGA_MOE_ERR_UNSUPPORTED)

@@ -1,0 +1,156 @@
+"""GPU parity of the whole layer on shapes the oracle finishes in seconds.
+
+Every intermediate the C ABI exposes is compared with the float64 oracle:
+dispatch metadata and pool copies bit-exact, re-quantised activations by the
+code rule, partials and y by relative Frobenius error (tests/gpu_util.py).
+Shapes span several tiles and ragged tails: pool blocks only partly filled,
+experts with several pool blocks, a single expert, top-1, inactive slots.
+"""
+
+import numpy as np
+import pytest
+
+from fp8_mixture_experts_amd import synthetic as S
+from oracle import moe
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny": S.WORKLOADS["tiny"],
+    "ragged": S.custom("ragged", tokens=37, hidden=384, intermediate=256, experts=5, topk=3,
+                       seed=3, weight_seed=4),
+    "one_expert": S.custom("one_expert", tokens=50, hidden=256, intermediate=128, experts=1,
+                           topk=1, seed=5, weight_seed=6),
+    "many_blocks": S.custom("many_blocks", tokens=300, hidden=256, intermediate=384, experts=3,
+                            topk=2, seed=9, weight_seed=10),
+    "skewed": S.custom("skewed", tokens=200, hidden=512, intermediate=256, experts=6, topk=2,
+                       routing="zipf", zipf_s=1.5, zero_experts=1, seed=13, weight_seed=14),
+}
+
+_cache = {}
+
+
+def _case(name):
+    if name not in _cache:
+        inp = S.make_inputs(SMALL[name])
+        _cache[name] = (inp, moe.forward(inp))
+    return _cache[name]
+
+
+def _compare_all(inp, ref, run, label):
+    T = inp["x"].shape[0]
+    v = run.views(T)
+    assert np.array_equal(v["counts"], ref["counts"]), label
+    assert np.array_equal(v["offsets"], ref["offsets"]), label
+    assert np.array_equal(v["slot_map"], ref["slot_map"]), label
+    assert np.array_equal(v["src"], ref["src"]), label
+    valid = ref["src"] >= 0
+    assert np.array_equal(v["l1_acts"][valid], ref["l1_acts"][valid]), label
+    assert np.array_equal(v["l1_sf"][:, valid], ref["l1_acts_sf"][:, valid]), label
+    assert np.array_equal(v["l1_w"][valid], ref["l1_w"][valid]), label
+    G.check_codes(v["l2_acts"][valid], ref["l2_acts"][valid], label)
+    G.check_sf(v["l2_sf"][:, valid], ref["l2_acts_sf"][:, valid], label)
+    act = ref["active"].reshape(-1)
+    assert G.rel_frobenius(v["comb"][act], ref["comb"][act]) <= 2e-3, label
+    return G.check_y(run.y(), ref["y"], label)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_matches_oracle(name):
+    inp, ref = _case(name)
+    run = G.Runner(inp)
+    try:
+        assert run.forward() == 0
+        err = _compare_all(inp, ref, run, name)
+        print(f"{name}: y rel frobenius {err:.2e}")
+    finally:
+        run.close()
+
+
+@pytest.mark.parametrize("name", ["ragged", "many_blocks", "skewed"])
+def test_block_m_and_l2_order_do_not_change_results(name):
+    inp, ref = _case(name)
+    outs = []
+    for bm in (32, 64, 128):
+        for nm in (0, 1):
+            run = G.Runner(inp, block_m=bm, l2_n_major=nm)
+            try:
+                assert run.forward() == 0
+                outs.append(((bm, nm), run.y().copy(), run.views(inp["x"].shape[0])["l2_acts"]))
+            finally:
+                run.close()
+    for key, y, l2 in outs[1:]:
+        assert np.array_equal(y, outs[0][1]), key
+        assert np.array_equal(l2, outs[0][2]), key
+    G.check_y(outs[0][1], ref["y"], name)
+
+
+def test_repeated_calls_are_bitwise_identical_and_leave_no_residue():
+    inp, ref = _case("many_blocks")
+    run = G.Runner(inp)
+    try:
+        assert run.forward() == 0
+        y1 = run.y().copy()
+        assert run.forward() == 0
+        assert np.array_equal(run.y(), y1)
+        # a smaller call on the same handle, then the full one again
+        small = dict(inp)
+        n = 41
+        for key in ("x", "x_sf", "topk_idx", "topk_weights"):
+            small[key] = inp[key][:n]
+        ref_small = moe.forward(small)
+        dev_small = G.to_device(small)
+        assert run.forward(dev_small) == 0
+        G.check_y(run.y(dev_small), ref_small["y"], "small call")
+        v = run.views(n)
+        assert np.array_equal(v["counts"], ref_small["counts"])
+        assert np.array_equal(v["src"], ref_small["src"])
+        assert run.forward() == 0
+        assert np.array_equal(run.y(), y1)
+    finally:
+        run.close()
+
+
+def test_inactive_invalid_and_duplicate_slots():
+    inp, _ = _case("ragged")
+    inp = dict(inp)
+    idx = inp["topk_idx"].copy()
+    idx[0, :] = -1                 # a token with no active slot -> y = +0
+    idx[1, 1] = idx[1, 0]          # the same expert twice
+    idx[2, 2] = -7
+    idx[3, 0] = 99                 # not a local expert: flagged and skipped
+    inp["topk_idx"] = idx
+    ref = moe.forward(inp)
+    run = G.Runner(inp)
+    try:
+        status = run.forward()
+        assert status == G.B.MEGA_MOE_DEVERR_BAD_EXPERT
+        assert run.layer.status() == 0           # sticky bit was cleared by the read
+        y = run.y()
+        assert np.all(y[0] == 0)
+        _compare_all(inp, ref, run, "edge slots")
+    finally:
+        run.close()
+
+
+def test_zero_tokens_is_a_no_op():
+    inp, _ = _case("tiny")
+    run = G.Runner(inp)
+    try:
+        before = run.y().copy()
+        assert run.forward(num_tokens=0) == 0
+        assert np.array_equal(run.y(), before)
+    finally:
+        run.close()
+
+
+def test_too_many_tokens_is_rejected():
+    inp, _ = _case("tiny")
+    run = G.Runner(inp, max_tokens=8)
+    try:
+        with pytest.raises(G.B.MegaMoEError) as ei:
+            run.forward()
+        assert ei.value.code == G.B.MEGA_MOE_ERR_INVALID_ARG
+    finally:
+        run.close()
