@@ -16,10 +16,18 @@
 // whatever the number of co-resident workgroups; it is still bounded by a
 // spin limit that raises MEGA_MOE_DEVERR_WAIT_TIMEOUT.
 //
-// Matrix core use (CDNA4): v_mfma_f32_32x32x64_f8f6f4, FP8 E4M3 operands.
-// A 128-K step is two 64-K MFMAs.  Scales are applied on the float
-// accumulators: L1 promotes once per 128-K block (acc += (sa*sw) * D), L2 once
-// per 64-K half (acc += (sa_half*sw) * D_half), as 5.3 and 5.4 describe.
+// Matrix core use (CDNA4).  The FP8 MFMA of gfx950 does not sum its
+// products exactly: within a group of adjacent K it aligns them to the
+// largest with fewer than 18 bits, so 448*448 + 1 loses the 1 (measured).
+// The L1 output is re-quantised to FP8 and must reproduce the exact-dot
+// codes, so the L1 GEMM converts its FP8 operand fragments to F16 in
+// registers (v_cvt_scalef32_pk_f16_fp8, exact for every E4M3 value) and runs
+// v_mfma_f32_32x32x16_f16, whose products are exact and whose sums round in
+// float32.  The L2 result only feeds BF16 partials and stays on
+// v_mfma_f32_32x32x64_f8f6f4 with FP8 operands.  Scales are applied on the
+// float accumulators: L1 promotes once per 128-K block (acc += (sa*sw) * D),
+// L2 once per 64-K half (acc += (sa_half*sw) * D_half), as 5.3 and 5.4
+// describe.
 // Each wave streams its own operand fragments straight from global memory
 // into registers (one 128-K step ahead), so the K loop has no LDS traffic and
 // no workgroup barrier; LDS is used only by the epilogues.
@@ -32,10 +40,16 @@ namespace mega_moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c) {
     // scale operands 0 select the plain (unscaled) FP8 x FP8 instruction
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ v16f mfma_f16(const v8h& a, const v8h& b, const v16f& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Operand fragment of one 32-row (A) or 32-column (B) slice for one 128-K
@@ -57,6 +71,27 @@ __device__ __forceinline__ void load_frag(Frag& f, const uint8_t* row, bool vali
     } else {
         f.h[0] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
         f.h[1] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+}
+
+// The 64 FP8 values a lane holds for one 128-K step, as 8 groups of 8 F16
+// (one 16-K F16 MFMA operand each).  Which K goes to which group does not
+// matter as long as A and B convert alike: each group of 8 MFMAs still sums
+// all 128 products of the step.
+struct HFrag {
+    v8h q[8];
+};
+
+__device__ __forceinline__ void to_f16(HFrag& o, const Frag& f) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int d0 = f.h[q >> 2][(q & 3) * 2];
+        const int d1 = f.h[q >> 2][(q & 3) * 2 + 1];
+        const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
+        const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
+        const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
+        const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
+        o.q[q] = v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
     }
 }
 
@@ -175,16 +210,22 @@ __device__ void l1_tile(const MoeArgs& a, Smem<BM, NWM>& sm, int e, int pb, int 
             for (int s = 0; s < 2; ++s) load_frag(nbf[s], brow[s] + (kb + 1) * BK, true);
         }
         const float sw = sw_base[kb];
+        HFrag hb[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) to_f16(hb[s], fb[s]);
 #pragma unroll
         for (int i = 0; i < C::kMS; ++i) {
             float sa[16];
             load_row_vec(sa, a.l1_sf + (size_t)kb * P + row0 + slice0[i]);
 #pragma unroll
             for (int v = 0; v < 16; ++v) sa[v] *= sw;
+            HFrag ha;
+            to_f16(ha, fa[i]);
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                v16f d = mfma_f8(fa[i].h[0], fb[s].h[0], zero);
-                d = mfma_f8(fa[i].h[1], fb[s].h[1], d);
+                v16f d = mfma_f16(ha.q[0], hb[s].q[0], zero);
+#pragma unroll
+                for (int q = 1; q < 8; ++q) d = mfma_f16(ha.q[q], hb[s].q[q], d);
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][s][v] = fmaf(d[v], sa[v], acc[i][s][v]);
             }

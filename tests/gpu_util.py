@@ -112,8 +112,10 @@ def check_codes(got, want, label=""):
         return 1.0
     diff = np.abs(ordered_codes(got) - ordered_codes(want))
     same = float(np.mean(diff == 0))
-    assert diff.max() <= 1, f"{label}: code off by {diff.max()} steps"
-    assert same >= 0.999, f"{label}: only {same:.5f} of codes identical"
+    msg = (f"{label}: {same:.6f} of {diff.size} codes identical, max step {diff.max()}, "
+           f"{int(np.sum(diff > 1))} codes off by more than one step")
+    assert diff.max() <= 1, msg
+    assert same >= 0.999, msg
     return same
 
 
