@@ -46,13 +46,14 @@ int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 // Sizes that depend only on the configuration.
 struct Layout {
     int64_t R_max, P_cap, PB_cap, chunks_max;
-    int64_t off[17];
+    int64_t off[19];
     int64_t total;
 };
 
 enum {
     L_COUNTS, L_OFFSETS, L_MBSTART, L_PBEXP, L_SLOTMAP, L_SRC, L_CHIST, L_CBASE,
-    L_L1ACTS, L_L1SF, L_L1W, L_L2ACTS, L_L2SF, L_COMB, L_READY, L_CTRL, L_COUNT
+    L_L1ACTS, L_L1SF, L_L1W, L_L2ACTS, L_L2SF, L_COMB, L_READY, L_XCDPBS, L_XCDINFO, L_CTRL,
+    L_COUNT
 };
 
 int check_config(const mega_moe_config* c) {
@@ -66,6 +67,10 @@ int check_config(const mega_moe_config* c) {
     if (c->intermediate <= 0 || c->intermediate % 128)
         return fail(MEGA_MOE_ERR_INVALID_ARG,
                     "intermediate must be a positive multiple of 128, got %d", c->intermediate);
+    if (c->hidden > 8192 || c->intermediate > 4096)
+        return fail(MEGA_MOE_ERR_UNSUPPORTED,
+                    "built for hidden <= 8192 and intermediate <= 4096 (got %d, %d)", c->hidden,
+                    c->intermediate);
     if (c->num_topk < 1) return fail(MEGA_MOE_ERR_INVALID_ARG, "num_topk must be >= 1");
     if (c->max_tokens < 0) return fail(MEGA_MOE_ERR_INVALID_ARG, "max_tokens must be >= 0");
     if ((int64_t)c->max_tokens * c->num_topk > (int64_t)1 << 30)
@@ -105,6 +110,8 @@ Layout make_layout(const mega_moe_config& c) {
     sz[L_L2SF] = (I / 64) * L.P_cap * 4;
     sz[L_COMB] = L.R_max * H * 2;
     sz[L_READY] = L.PB_cap * 4;
+    sz[L_XCDPBS] = L.PB_cap * 4;
+    sz[L_XCDINFO] = 2 * MAX_XCD * 4;
     sz[L_CTRL] = sizeof(MoeCtrl);
     int64_t o = 0;
     for (int i = 0; i < L_COUNT; ++i) {
@@ -226,6 +233,9 @@ int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out) {
     a.nb1 = 2 * cfg->intermediate / 128;
     a.nb2 = cfg->hidden / 128;
     a.wait_spin_limit = 1u << 22;
+    // gfx950 groups 32 compute units per XCD, each XCD with its own L2
+    a.n_xcd = (h->num_cus % 32 == 0 && h->num_cus / 32 >= 1 && h->num_cus / 32 <= MAX_XCD)
+                  ? h->num_cus / 32 : 1;
     uint8_t* w = h->ws;
     a.counts = (int32_t*)(w + L.off[L_COUNTS]);
     a.offsets = (int32_t*)(w + L.off[L_OFFSETS]);
@@ -242,6 +252,8 @@ int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out) {
     a.l2_sf = (float*)(w + L.off[L_L2SF]);
     a.comb = (uint16_t*)(w + L.off[L_COMB]);
     a.ready = (uint32_t*)(w + L.off[L_READY]);
+    a.xcd_pbs = (int32_t*)(w + L.off[L_XCDPBS]);
+    a.xcd_info = (int32_t*)(w + L.off[L_XCDINFO]);
     a.ctrl = (MoeCtrl*)(w + L.off[L_CTRL]);
     h->last_T = 0;
     *out = h;
@@ -282,6 +294,7 @@ int mega_moe_forward(mega_moe_handle* h, int32_t T, const uint8_t* x, const floa
     a.R = T * h->cfg.num_topk;
     a.block_m = p.block_m;
     a.n_major = p.l2_n_major;
+    a.xcd_group = p.block_m == 32 ? 4 : (p.block_m == 64 ? 2 : 4);
     a.num_chunks = (a.R + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK;
     a.x = x;
     a.x_sf = x_sf;

@@ -122,7 +122,7 @@ moe_dispatch_scan(MoeArgs a) {
         a.offsets[E] = total_rows;
         a.mb_start[E] = total_mb;
         a.ctrl->total_mb = total_mb;
-        a.ctrl->next_tile = 0;
+        for (int x = 0; x < MAX_XCD; ++x) a.ctrl->next_tile[x] = 0;
     }
     __syncthreads();
 
@@ -135,6 +135,42 @@ moe_dispatch_scan(MoeArgs a) {
         const int pad0 = s_off[ex] + s_count[ex];
         const int pad1 = s_off[ex + 1];
         for (int r = pad0 + tid; r < pad1; r += SCAN_THREADS) a.src[r] = -1;
+    }
+
+    // Per-XCD work lists: each expert's pool blocks are cut into chunks of at
+    // most xcd_group consecutive blocks, and the chunks (expert-major order)
+    // are dealt round-robin to the XCDs.  A chunk stays on one XCD, so its
+    // blocks share the expert's weight stream through that XCD's L2.
+    __shared__ int s_xcd[2 * MAX_XCD];
+    const int G = a.xcd_group;
+    if (tid < a.n_xcd) {
+        int n = 0, chunk = 0;
+        for (int ex = 0; ex < E; ++ex) {
+            const int mb = s_mb[ex + 1] - s_mb[ex];
+            for (int k0 = 0; k0 < mb; k0 += G, ++chunk)
+                if (chunk % a.n_xcd == tid) n += min(G, mb - k0);
+        }
+        s_xcd[MAX_XCD + tid] = n;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int start = 0;
+        for (int x = 0; x < a.n_xcd; ++x) {
+            s_xcd[x] = start;
+            start += s_xcd[MAX_XCD + x];
+        }
+    }
+    __syncthreads();
+    if (tid < a.n_xcd) {
+        int pos = s_xcd[tid], chunk = 0;
+        for (int ex = 0; ex < E; ++ex) {
+            const int mb0 = s_mb[ex], mb = s_mb[ex + 1] - mb0;
+            for (int k0 = 0; k0 < mb; k0 += G, ++chunk)
+                if (chunk % a.n_xcd == tid)
+                    for (int t = k0; t < min(k0 + G, mb); ++t) a.xcd_pbs[pos++] = mb0 + t;
+        }
+        a.xcd_info[2 * tid] = s_xcd[tid];
+        a.xcd_info[2 * tid + 1] = s_xcd[MAX_XCD + tid];
     }
 
     // expert of every pool block, and a cleared arrival counter for it

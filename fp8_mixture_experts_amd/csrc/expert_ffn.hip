@@ -5,16 +5,23 @@
 // route ("MegaMoE SM90 Implementation Design (Final)" 3.3 phases 2-3, 5.1-5.4,
 // 10.1, 11.1, 12).
 //
-// Work is a queue of tiles of BLOCK_M pool rows x 128 output columns: first
-// every L1 tile (pool block pb, 128 interleaved W1 rows = 64 outputs = one
-// per-64 scale group), then every L2 tile (pool block pb, 128 columns of H).
-// Workgroups take tiles in queue order with one atomic each.  An L2 tile of pb
-// waits until all 2I/128 L1 tiles of pb have published their output through
-// an arrival counter (the role of the L2 arrival mask of 14.3).  L1 tiles
-// never wait and every L2 tile depends only on tiles that precede it in the
-// queue, which running workgroups already own, so the wait always ends,
-// whatever the number of co-resident workgroups; it is still bounded by a
-// spin limit that raises MEGA_MOE_DEVERR_WAIT_TIMEOUT.
+// Work is tiles of BLOCK_M pool rows x 128 output columns: L1 tiles (pool
+// block pb, 128 interleaved W1 rows = 64 outputs = one per-64 scale group) and
+// L2 tiles (pool block pb, 128 columns of H).  The dispatch gives every XCD
+// (accelerator die, each with its own L2) a list of pool blocks, in chunks of
+// at most xcd_group blocks of one expert, and every XCD keeps one queue: first
+// the L1 tiles of its pool blocks, then their L2 tiles.  A workgroup reads its XCD from the
+// XCC_ID hardware register and takes tiles from that queue with one atomic
+// each.  An L2 tile of pb waits until all 2I/128 L1 tiles of pb have published
+// their output through an arrival counter (the role of the L2 arrival mask of
+// 14.3).  Producer and consumer of pb share one XCD and so one L2: the
+// producer waits for its stores to be acknowledged before bumping the counter
+// and the consumer invalidates only its own CU's vector L1 before reading, so
+// no device-wide L2 write-back or invalidation is needed.  L1 tiles never wait
+// and every L2 tile depends only on tiles that precede it in its queue, which
+// running workgroups of the same XCD already own, so the wait always ends,
+// whatever the number of co-resident workgroups; it is still bounded by a spin
+// limit that raises MEGA_MOE_DEVERR_WAIT_TIMEOUT.
 //
 // Matrix core use (CDNA4).  The FP8 MFMA of gfx950 does not sum its
 // products exactly: within a group of adjacent K it aligns them to the
@@ -28,9 +35,20 @@
 // float accumulators: L1 promotes once per 128-K block (acc += (sa*sw) * D),
 // L2 once per 64-K half (acc += (sa_half*sw) * D_half), as 5.3 and 5.4
 // describe.
-// Each wave streams its own operand fragments straight from global memory
-// into registers (one 128-K step ahead), so the K loop has no LDS traffic and
-// no workgroup barrier; LDS is used only by the epilogues.
+//
+// Memory pipeline.  A workgroup is 4 waves.  Each 128-K step of the tile's
+// operands (BLOCK_M activation rows and 128 weight rows, 128 bytes each) is
+// fetched with fully coalesced 16-byte buffer loads (8 lanes per 128-byte
+// row) into a ring of DEPTH register stages, written to one of two LDS
+// buffers in the MFMA operand layout (XOR-swizzled so both the writes and the
+// fragment reads are free of bank conflicts), and consumed after one
+// workgroup barrier.  Wave w computes output columns [32w, 32w+32) of the
+// tile over all its rows and the whole K step, so no partial sums cross waves.
+// In L1 those 32 stored W1 rows are four interleave groups of 8 (gate, up,
+// gate, up), so the gate and up values of an output sit in lanes c and c+8 of
+// one wave and meet through one swizzle.  The tile's per-row activation scales
+// and per-block weight scales are staged in LDS once per tile; 32-row slices
+// that hold no routes are skipped.
 #include <hip/hip_runtime.h>
 
 #include "moe_args.h"
@@ -38,10 +56,17 @@
 
 namespace mega_moe {
 
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+constexpr int BN = 128;              // output columns per tile
+constexpr int BK = 128;              // K bytes per step
+constexpr int NT = 256;              // threads per workgroup (4 waves)
+constexpr int DEPTH = 3;             // register stages of the global-load ring
+constexpr int MAX_SF_GROUPS = 64;    // H/128 and I/64 per tile (H <= 8192, I <= 4096)
 
 __device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c) {
     // scale operands 0 select the plain (unscaled) FP8 x FP8 instruction
@@ -52,47 +77,61 @@ __device__ __forceinline__ v16f mfma_f16(const v8h& a, const v8h& b, const v16f&
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// Operand fragment of one 32-row (A) or 32-column (B) slice for one 128-K
-// step: half h holds K bytes [64h, 64h+64).  Lane l owns row l%32; its group
-// g = l/32 takes bytes 64h + 16g + [0,16) and 64h + 32 + 16g + [0,16) of the
-// half.  A and B use the same K placement, so each MFMA sums exactly the 64
-// products of its half.
+// Buffer resource over `bytes` bytes at `base` (gfx9 word 3: raw 32-bit data).
+// Loads whose per-lane offset lies beyond the range return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// ---------------------------------------------------------------------------
+// Operand layout.  The MFMA operand of one 32-row (A) or 32-column (B) slice
+// for a 64-K half h: lane L = r + 32g holds row r, K bytes 64h + 32p + 16g +
+// [0,16) for p = 0, 1 (A and B alike, so each MFMA sums exactly the products
+// of its half).  In LDS a step stores, per slice s, half h and part p, one
+// 1 KB block of 64 lanes x 16 bytes; lane L's granule sits at L ^ 2c, where
+// c = 4h + 2p + g is the 16-byte chunk of the row it came from.  The swizzle
+// spreads the coalesced writes (8 chunks of 8 rows) and the fragment reads (64
+// lanes of one block) evenly over the LDS banks.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lds_granule(int n, int c) {
+    const int s = n >> 5, r = n & 31;
+    const int h = c >> 2, p = (c >> 1) & 1, g = c & 1;
+    return ((s * 2 + h) * 2 + p) * 64 + ((r + 32 * g) ^ (2 * c));
+}
+
+// Fragment of slice s, half h for this lane from an operand region of LDS.
+__device__ __forceinline__ v8i read_frag(const uint8_t* region, int s, int h) {
+    const int L = threadIdx.x & 63;
+    const int g = L >> 5;
+    v4i q[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int c = 4 * h + 2 * p + g;
+        const int gi = ((s * 2 + h) * 2 + p) * 64 + (L ^ (2 * c));
+        q[p] = *reinterpret_cast<const v4i*>(region + gi * 16);
+    }
+    return v8i{q[0][0], q[0][1], q[0][2], q[0][3], q[1][0], q[1][1], q[1][2], q[1][3]};
+}
+
+// Both 64-K halves of slice s: dwords 0-7 half 0, dwords 8-15 half 1.
 struct Frag {
     v8i h[2];
 };
 
-__device__ __forceinline__ void load_frag(Frag& f, const uint8_t* row, bool valid) {
-    if (valid) {
-        const int g = (threadIdx.x >> 5) & 1;
-        const uint4* p = reinterpret_cast<const uint4*>(row) + g;
-        const uint4 q0 = p[0], q1 = p[2], q2 = p[4], q3 = p[6];
-        f.h[0] = v8i{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
-        f.h[1] = v8i{(int)q2.x, (int)q2.y, (int)q2.z, (int)q2.w, (int)q3.x, (int)q3.y, (int)q3.z, (int)q3.w};
-    } else {
-        f.h[0] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        f.h[1] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+__device__ __forceinline__ Frag read_frag2(const uint8_t* region, int s) {
+    return Frag{read_frag(region, s, 0), read_frag(region, s, 1)};
 }
 
-// The 64 FP8 values a lane holds for one 128-K step, as 8 groups of 8 F16
-// (one 16-K F16 MFMA operand each).  Which K goes to which group does not
-// matter as long as A and B convert alike: each group of 8 MFMAs still sums
-// all 128 products of the step.
-struct HFrag {
-    v8h q[8];
-};
-
-__device__ __forceinline__ void to_f16(HFrag& o, const Frag& f) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int d0 = f.h[q >> 2][(q & 3) * 2];
-        const int d1 = f.h[q >> 2][(q & 3) * 2 + 1];
-        const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
-        const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
-        const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
-        const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
-        o.q[q] = v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-    }
+// Eight FP8 values (dwords 2q, 2q+1 of a half fragment) as one 16-K F16
+// operand.  A and B convert alike, so the four F16 MFMAs of a half still sum
+// all 64 of its products.
+__device__ __forceinline__ v8h f16_part(const v8i& f, int q) {
+    const int d0 = f[2 * q], d1 = f[2 * q + 1];
+    const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
+    const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
+    const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
+    const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
+    return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // Accumulator layout of the 32x32 MFMA: register v of lane l holds row
@@ -102,7 +141,8 @@ __device__ __forceinline__ int acc_row(int v) {
     return 8 * (v >> 2) + 4 * ((threadIdx.x >> 5) & 1) + (v & 3);
 }
 
-__device__ __forceinline__ void load_row_vec(float (&out)[16], const float* base) {
+template <typename T>
+__device__ __forceinline__ void load_row_vec(float (&out)[16], const T* base) {
     const int g4 = 4 * ((threadIdx.x >> 5) & 1);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -114,11 +154,36 @@ __device__ __forceinline__ void load_row_vec(float (&out)[16], const float* base
     }
 }
 
+// Per-row vector in accumulator layout (four float4 runs) as one v16f.
+__device__ __forceinline__ v16f row_vec(const float* base) {
+    const int g4 = 4 * ((threadIdx.x >> 5) & 1);
+    const float4 a = *reinterpret_cast<const float4*>(base + g4);
+    const float4 b = *reinterpret_cast<const float4*>(base + 8 + g4);
+    const float4 c = *reinterpret_cast<const float4*>(base + 16 + g4);
+    const float4 d = *reinterpret_cast<const float4*>(base + 24 + g4);
+    return v16f{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
+}
+
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
     if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
     u += 0x7fffu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
+}
+
+// Maximum over the 32 lanes that share bit 5 of the lane id: DPP xor-1 and
+// xor-2 within quads, the half-row and row mirrors, then a swizzle xor 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row_max32(float m) {
+    m = fmaxf(m, dpp_move<0xB1>(m));    // quad_perm [1,0,3,2]
+    m = fmaxf(m, dpp_move<0x4E>(m));    // quad_perm [2,3,0,1]
+    m = fmaxf(m, dpp_move<0x141>(m));   // row_half_mirror
+    m = fmaxf(m, dpp_move<0x140>(m));   // row_mirror
+    return fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x401F)));
 }
 
 // OCP E4M3 code of v (|v| <= 448 after the clamp), round to nearest even.
@@ -127,185 +192,256 @@ __device__ __forceinline__ uint8_t e4m3_code(float v) {
     return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xff);
 }
 
-constexpr int BN = 128;         // output columns per tile
-constexpr int BK = 128;         // K bytes per step
-
-template <int BM, int NWM>
-struct TileCfg {
-    static constexpr int kWaves = NWM * 2;            // 2 waves across the 128 columns
-    static constexpr int kThreads = kWaves * 64;
-    static constexpr int kMS = BM / (32 * NWM);       // 32-row slices per wave
-    static_assert(kMS >= 1 && kMS * 32 * NWM == BM, "bad tile");
+template <int MS>
+struct Cfg {
+    static constexpr int BM = 32 * MS;                     // pool rows per tile
+    static constexpr int A_BYTES = BM * BK;                // A part of one step
+    static constexpr int STEP_BYTES = A_BYTES + BN * BK;   // A + B of one step
+    static constexpr int CHUNKS = STEP_BYTES / 16;
+    static constexpr int PER_THREAD = CHUNKS / NT;         // 16-byte loads per thread per step
+    static_assert(PER_THREAD * NT == CHUNKS && (A_BYTES / 16) == MS * NT, "step split");
+    // LDS map: two step buffers, then scales.  After the K loop the buffers
+    // hold the cross-half reduction and then the epilogue staging.
+    static constexpr int OFF_SF = 2 * STEP_BYTES;
+    static constexpr int SF_BYTES = MAX_SF_GROUPS * BM * 4 + MAX_SF_GROUPS * 4 + BM * 4;
+    static constexpr int LDS_BYTES = OFF_SF + SF_BYTES + 16;
+    static_assert(BM * BN * 4 <= 2 * STEP_BYTES, "reduction buffer");
 };
 
-template <int BM, int NWM>
-struct Smem {
-    union {
-        struct {
-            float amax[2][BM];
-            uint8_t codes[BM][64];
-        } l1;
-        uint16_t l2_stage[BM][BN];
-    };
-    int tile;
+template <int MS>
+struct Lds {
+    uint8_t* base;
+    __device__ uint8_t* step(int b) const { return base + b * Cfg<MS>::STEP_BYTES; }
+    __device__ float* a_sf(int g) const {
+        return reinterpret_cast<float*>(base + Cfg<MS>::OFF_SF) + g * Cfg<MS>::BM;
+    }
+    __device__ float* w_sf() const {
+        return reinterpret_cast<float*>(base + Cfg<MS>::OFF_SF) + MAX_SF_GROUPS * Cfg<MS>::BM;
+    }
+    __device__ float* row_w() const {   // top-k weight of each row (L1 tiles)
+        return w_sf() + MAX_SF_GROUPS;
+    }
+    __device__ int* tile() const {
+        return reinterpret_cast<int*>(base + Cfg<MS>::OFF_SF + Cfg<MS>::SF_BYTES);
+    }
+    __device__ float* red() const { return reinterpret_cast<float*>(base); }
 };
+
+// This thread's share of every step: chunk j < MS belongs to A row
+// tid/8 + 32j, the rest to B row tid/8 + 32(j-MS); chunk column tid%8.
+template <int MS>
+struct Loader {
+    int voff[Cfg<MS>::PER_THREAD];
+    int lds[Cfg<MS>::PER_THREAD];
+    __amdgpu_buffer_rsrc_t ra, rb;
+
+    __device__ Loader(__amdgpu_buffer_rsrc_t ra_, int a_row_bytes, __amdgpu_buffer_rsrc_t rb_,
+                      int b_row_bytes)
+        : ra(ra_), rb(rb_) {
+        const int t = threadIdx.x;
+        const int c = t & 7;
+#pragma unroll
+        for (int j = 0; j < Cfg<MS>::PER_THREAD; ++j) {
+            if (j < MS) {
+                const int n = (t >> 3) + 32 * j;
+                voff[j] = n * a_row_bytes + 16 * c;
+                lds[j] = lds_granule(n, c) * 16;
+            } else {
+                const int n = (t >> 3) + 32 * (j - MS);
+                voff[j] = n * b_row_bytes + 16 * c;
+                lds[j] = Cfg<MS>::A_BYTES + lds_granule(n, c) * 16;
+            }
+        }
+    }
+    __device__ __forceinline__ void load(v4i (&r)[Cfg<MS>::PER_THREAD], int kb) const {
+#pragma unroll
+        for (int j = 0; j < Cfg<MS>::PER_THREAD; ++j)
+            r[j] = __builtin_amdgcn_raw_buffer_load_b128(j < MS ? ra : rb, voff[j], kb * BK, 0);
+    }
+    __device__ __forceinline__ void store(uint8_t* step, const v4i (&r)[Cfg<MS>::PER_THREAD]) const {
+#pragma unroll
+        for (int j = 0; j < Cfg<MS>::PER_THREAD; ++j)
+            *reinterpret_cast<v4i*>(step + lds[j]) = r[j];
+    }
+};
+
+// K loop: DEPTH register stages in flight, two LDS buffers, one barrier per
+// step.  The body has no data-dependent branch, so the compiler waits only
+// for the stage it stores; the last steps re-fetch step KB-1 (cache hits).
+template <int MS, typename Compute>
+__device__ __forceinline__ void k_loop(const Loader<MS>& ld, const Lds<MS>& lds, int KB,
+                                       Compute&& compute) {
+    v4i st[DEPTH][Cfg<MS>::PER_THREAD];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) ld.load(st[d], min(d, KB - 1));
+    int kb = 0;
+    for (; kb + DEPTH <= KB; kb += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            uint8_t* buf = lds.step((kb + d) & 1);
+            ld.store(buf, st[d]);
+            __syncthreads();
+            ld.load(st[d], min(kb + d + DEPTH, KB - 1));
+            compute(buf, kb + d);
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d) {
+        if (kb + d < KB) {
+            uint8_t* buf = lds.step((kb + d) & 1);
+            ld.store(buf, st[d]);
+            __syncthreads();
+            compute(buf, kb + d);
+        }
+    }
+}
+
+template <int N>
+struct IntTag {
+    static constexpr int value = N;
+};
+
+// Runs fn(IntTag<act>) for the active slice count (1..MS).
+template <int MS, typename Fn>
+__device__ __forceinline__ void dispatch_act(int act, Fn&& fn) {
+    if constexpr (MS >= 4) {
+        if (act == 4) { fn(IntTag<4>{}); return; }
+        if (act == 3) { fn(IntTag<3>{}); return; }
+    }
+    if constexpr (MS >= 2) {
+        if (act == 2) { fn(IntTag<2>{}); return; }
+    }
+    fn(IntTag<1>{});
+}
+
+template <int MS>
+__device__ __forceinline__ void stage_scales(const Lds<MS>& lds, const float* a_base, size_t P,
+                                             int a_groups, const float* w_base, int w_groups,
+                                             int row0) {
+    constexpr int BM = Cfg<MS>::BM;
+    for (int i = threadIdx.x; i < a_groups * BM; i += NT) {
+        const int g = i / BM;
+        const int r = i - g * BM;
+        lds.a_sf(g)[r] = a_base[(size_t)g * P + row0 + r];
+    }
+    for (int i = threadIdx.x; i < w_groups; i += NT) lds.w_sf()[i] = w_base[i];
+}
 
 // ---------------------------------------------------------------------------
 // L1 tile: pool rows [row0, row0 + valid) of expert e, W1 N block nb.
 // ---------------------------------------------------------------------------
-template <int BM, int NWM>
-__device__ void l1_tile(const MoeArgs& a, Smem<BM, NWM>& sm, int e, int pb, int row0,
-                        int valid, int nb) {
-    using C = TileCfg<BM, NWM>;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave / 2, wn = wave % 2;
-    const int c = lane & 31;
+template <int MS>
+__device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int row0, int valid,
+                        int nb) {
+    constexpr int BM = Cfg<MS>::BM;
     const int H = a.H;
     const int KB = H / BK;
     const size_t P = a.P_cap;
+    const int w = threadIdx.x >> 6;
+    const int c = threadIdx.x & 31;
+    const int act = min(MS, (valid + 31) / 32);
 
-    // A rows of this lane, one per 32-row slice
-    const uint8_t* arow[C::kMS];
-    bool avalid[C::kMS];
-    int slice0[C::kMS];
-#pragma unroll
-    for (int i = 0; i < C::kMS; ++i) {
-        slice0[i] = (wm * C::kMS + i) * 32;
-        const int r = slice0[i] + c;
-        avalid[i] = r < valid;
-        arow[i] = a.l1_acts + (size_t)(row0 + r) * H;
-    }
-    // B rows: slice 0 = gate rows, slice 1 = up rows of outputs 32*wn + c
-    const uint8_t* w1e = a.w1 + (size_t)e * (2 * a.I) * H;
-    const uint8_t* brow[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const int n = nb * BN + wn * 64 + 16 * (c >> 3) + 8 * s + (c & 7);
-        brow[s] = w1e + (size_t)n * H;
-    }
-    const float* sw_base = a.w1_sf + ((size_t)e * a.nb1 + nb) * KB;
+    stage_scales(lds, a.l1_sf, P, KB, a.w1_sf + ((size_t)e * a.nb1 + nb) * KB, KB, row0);
+    for (int r = threadIdx.x; r < BM; r += NT) lds.row_w()[r] = a.l1_w[row0 + r];
+    const Loader<MS> ld(make_rsrc(a.l1_acts + (size_t)row0 * H, (uint32_t)valid * H), H,
+                        make_rsrc(a.w1 + ((size_t)e * (2 * a.I) + (size_t)nb * BN) * H,
+                                  (uint32_t)BN * H),
+                        H);
 
-    v16f acc[C::kMS][2];
+    v16f acc[MS];
 #pragma unroll
-    for (int i = 0; i < C::kMS; ++i)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) acc[i][s] = v16f{};
+    for (int i = 0; i < MS; ++i) acc[i] = v16f{};
     const v16f zero = v16f{};
 
-    Frag fa[C::kMS], fb[2];
+    dispatch_act<MS>(act, [&](auto tag) {
+        constexpr int ACT = decltype(tag)::value;
+        k_loop<MS>(ld, lds, KB, [&](const uint8_t* buf, int kb) {
+            const float sw = lds.w_sf()[kb];
+            const Frag fb = read_frag2(buf + Cfg<MS>::A_BYTES, w);
 #pragma unroll
-    for (int i = 0; i < C::kMS; ++i) load_frag(fa[i], arow[i], avalid[i]);
+            for (int i = 0; i < ACT; ++i) {
+                const Frag fa = read_frag2(buf, i);
+                v16f d = mfma_f16(f16_part(fa.h[0], 0), f16_part(fb.h[0], 0), zero);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) load_frag(fb[s], brow[s], true);
+                for (int q = 1; q < 8; ++q)
+                    d = mfma_f16(f16_part(fa.h[q >> 2], q & 3), f16_part(fb.h[q >> 2], q & 3), d);
+                const v16f sa = row_vec(lds.a_sf(kb) + 32 * i) * sw;
+                acc[i] = __builtin_elementwise_fma(d, sa, acc[i]);
+            }
+        });
+    });
+    __syncthreads();                    // every wave is done with the step buffers
 
-    for (int kb = 0; kb < KB; ++kb) {
-        Frag na[C::kMS], nbf[2];
-        const bool more = kb + 1 < KB;
-        if (more) {
+    // ---- epilogue: SwiGLU x top-k weight, row amax, FP8 ----
+    // Lane c < 8 (mod 16) holds a gate value, lane c + 8 the up value of the
+    // same output, 16w + 8*(c/16) + c%8 of the tile's 64.  silu(g) = g / (1 +
+    // 2^(-g*log2 e)) with the hardware exp2 and reciprocal (a few float32 ulps;
+    // the code rule tolerates them); the row amax runs over the wave by DPP
+    // and one swizzle, then over the four waves via LDS.  The scale is the
+    // exactly rounded amax / 448 the method stores; h / sf is taken as
+    // h * (1 / sf).
+    float* amax = lds.red();                                   // [4][BM]
+    const bool gate_lane = (c & 8) == 0;
+    float h[MS][16];
 #pragma unroll
-            for (int i = 0; i < C::kMS; ++i) load_frag(na[i], arow[i] + (kb + 1) * BK, avalid[i]);
+    for (int i = 0; i < MS; ++i) {
+        if (i >= act) break;
+        const v16f wt = row_vec(lds.row_w() + 32 * i);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) load_frag(nbf[s], brow[s] + (kb + 1) * BK, true);
+        for (int v = 0; v < 16; ++v) {
+            const float x = acc[i][v];
+            const float y = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x201F));
+            const float ex = __builtin_amdgcn_exp2f(-x * 1.44269504088896340736f);
+            const float silu = x * __builtin_amdgcn_rcpf(1.0f + ex);
+            h[i][v] = gate_lane ? silu * y * wt[v] : 0.0f;
         }
-        const float sw = sw_base[kb];
-        HFrag hb[2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) to_f16(hb[s], fb[s]);
+        for (int v = 0; v < 16; ++v) {
+            const float m = row_max32(fabsf(h[i][v]));
+            if (c == 0) amax[w * BM + 32 * i + acc_row(v)] = m;
+        }
+    }
+    __syncthreads();
+    uint8_t* out = a.l2_acts + (size_t)row0 * a.I + nb * 64 + 16 * w + 8 * ((c >> 4) & 1) + (c & 7);
 #pragma unroll
-        for (int i = 0; i < C::kMS; ++i) {
-            float sa[16];
-            load_row_vec(sa, a.l1_sf + (size_t)kb * P + row0 + slice0[i]);
+    for (int i = 0; i < MS; ++i) {
+        if (i >= act) break;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) sa[v] *= sw;
-            HFrag ha;
-            to_f16(ha, fa[i]);
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                v16f d = mfma_f16(ha.q[0], hb[s].q[0], zero);
-#pragma unroll
-                for (int q = 1; q < 8; ++q) d = mfma_f16(ha.q[q], hb[s].q[q], d);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][s][v] = fmaf(d[v], sa[v], acc[i][s][v]);
+        for (int v = 0; v < 16; ++v) {
+            const int r = 32 * i + acc_row(v);
+            const float am = fmaxf(fmaxf(amax[r], amax[BM + r]), fmaxf(amax[2 * BM + r], amax[3 * BM + r]));
+            const float sf = am / 448.0f;
+            const float inv = sf > 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
+            if (r < valid) {
+                if (gate_lane) out[(size_t)r * a.I] = e4m3_code(h[i][v] * inv);
+                if (w == 0 && c == 0) a.l2_sf[(size_t)nb * P + row0 + r] = sf;
             }
         }
-        if (more) {
-#pragma unroll
-            for (int i = 0; i < C::kMS; ++i) fa[i] = na[i];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) fb[s] = nbf[s];
-        }
     }
-
-    // ---- epilogue: SwiGLU x top-k weight, row amax over the 64 outputs ----
-    float h[C::kMS][16];
-#pragma unroll
-    for (int i = 0; i < C::kMS; ++i) {
-        float w[16];
-        load_row_vec(w, a.l1_w + row0 + slice0[i]);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float g = acc[i][0][v];
-            const float u = acc[i][1][v];
-            const float silu = g / (1.0f + expf(-g));
-            h[i][v] = silu * u * w[v];
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            float m = fabsf(h[i][v]);
-#pragma unroll
-            for (int d = 1; d < 32; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
-            if (c == 0) sm.l1.amax[wn][slice0[i] + acc_row(v)] = m;
-        }
-    }
+    // publish: the vector L1 writes through, so once every thread's stores are
+    // acknowledged they sit in this XCD's L2, where the consumer reads them
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < C::kMS; ++i) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = slice0[i] + acc_row(v);
-            const float amax = fmaxf(sm.l1.amax[0][r], sm.l1.amax[1][r]);
-            const float sf = amax / 448.0f;
-            const float q = sf > 0.0f ? h[i][v] / sf : 0.0f;
-            sm.l1.codes[r][wn * 32 + c] = e4m3_code(q);
-            if (wn == 0 && c == 0 && r < valid) a.l2_sf[(size_t)nb * P + row0 + r] = sf;
-        }
-    }
-    __syncthreads();
-    // coalesced store of the BM x 64 FP8 block (16 bytes per thread)
-    for (int q = tid; q < BM * 4; q += C::kThreads) {
-        const int r = q >> 2, part = q & 3;
-        if (r < valid) {
-            const uint4 v = *reinterpret_cast<const uint4*>(&sm.l1.codes[r][part * 16]);
-            *reinterpret_cast<uint4*>(a.l2_acts + (size_t)(row0 + r) * a.I + nb * 64 + part * 16) = v;
-        }
-    }
-    // publish: every thread's stores reach the device coherence point before
-    // the arrival counter of this pool block moves
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (tid == 0) __hip_atomic_fetch_add(&a.ready[pb], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(&a.ready[pb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
 // L2 tile: pool rows [row0, row0 + valid) of expert e, W2 N block nb.
 // ---------------------------------------------------------------------------
-template <int BM, int NWM>
-__device__ void l2_tile(const MoeArgs& a, Smem<BM, NWM>& sm, int e, int pb, int row0,
-                        int valid, int nb) {
-    using C = TileCfg<BM, NWM>;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave / 2, wn = wave % 2;
-    const int c = lane & 31;
+template <int MS>
+__device__ void l2_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int row0, int valid,
+                        int nb) {
+    constexpr int BM = Cfg<MS>::BM;
     const int I = a.I;
     const int KB = I / BK;
     const size_t P = a.P_cap;
+    const int w = threadIdx.x >> 6;
+    const int c = threadIdx.x & 31;
+    const int act = min(MS, (valid + 31) / 32);
 
     // wait until every L1 tile of this pool block has published
-    if (tid == 0) {
+    if (threadIdx.x == 0) {
         uint32_t spins = 0;
         while (__hip_atomic_load(&a.ready[pb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                (uint32_t)a.nb1) {
@@ -317,157 +453,129 @@ __device__ void l2_tile(const MoeArgs& a, Smem<BM, NWM>& sm, int e, int pb, int 
         }
     }
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // drop this CU's vector L1 lines so the L1 tiles' output is read from L2
+    asm volatile("buffer_inv sc0" ::: "memory");
 
-    const uint8_t* arow[C::kMS];
-    bool avalid[C::kMS];
-    int slice0[C::kMS];
-#pragma unroll
-    for (int i = 0; i < C::kMS; ++i) {
-        slice0[i] = (wm * C::kMS + i) * 32;
-        const int r = slice0[i] + c;
-        avalid[i] = r < valid;
-        arow[i] = a.l2_acts + (size_t)(row0 + r) * I;
-    }
-    const uint8_t* w2e = a.w2 + (size_t)e * a.H * I;
-    const uint8_t* brow[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) brow[s] = w2e + (size_t)(nb * BN + wn * 64 + s * 32 + c) * I;
-    const float* sw_base = a.w2_sf + ((size_t)e * a.nb2 + nb) * KB;
+    stage_scales(lds, a.l2_sf, P, 2 * KB, a.w2_sf + ((size_t)e * a.nb2 + nb) * KB, KB, row0);
+    const Loader<MS> ld(make_rsrc(a.l2_acts + (size_t)row0 * I, (uint32_t)valid * I), I,
+                        make_rsrc(a.w2 + ((size_t)e * a.H + (size_t)nb * BN) * I, (uint32_t)BN * I),
+                        I);
 
-    v16f acc[C::kMS][2];
+    v16f acc[MS];
 #pragma unroll
-    for (int i = 0; i < C::kMS; ++i)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) acc[i][s] = v16f{};
+    for (int i = 0; i < MS; ++i) acc[i] = v16f{};
     const v16f zero = v16f{};
 
-    Frag fa[C::kMS], fb[2];
+    dispatch_act<MS>(act, [&](auto tag) {
+        constexpr int ACT = decltype(tag)::value;
+        k_loop<MS>(ld, lds, KB, [&](const uint8_t* buf, int kb) {
+            const float sw = lds.w_sf()[kb];
+            const Frag fb = read_frag2(buf + Cfg<MS>::A_BYTES, w);
 #pragma unroll
-    for (int i = 0; i < C::kMS; ++i) load_frag(fa[i], arow[i], avalid[i]);
+            for (int i = 0; i < ACT; ++i) {
+                const Frag fa = read_frag2(buf, i);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) load_frag(fb[s], brow[s], true);
-
-    for (int kb = 0; kb < KB; ++kb) {
-        Frag na[C::kMS], nbf[2];
-        const bool more = kb + 1 < KB;
-        if (more) {
-#pragma unroll
-            for (int i = 0; i < C::kMS; ++i) load_frag(na[i], arow[i] + (kb + 1) * BK, avalid[i]);
-#pragma unroll
-            for (int s = 0; s < 2; ++s) load_frag(nbf[s], brow[s] + (kb + 1) * BK, true);
-        }
-        const float sw = sw_base[kb];
-#pragma unroll
-        for (int i = 0; i < C::kMS; ++i) {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                float sa[16];
-                load_row_vec(sa, a.l2_sf + (size_t)(2 * kb + hh) * P + row0 + slice0[i]);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) sa[v] *= sw;
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const v16f d = mfma_f8(fa[i].h[hh], fb[s].h[hh], zero);
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[i][s][v] = fmaf(d[v], sa[v], acc[i][s][v]);
+                for (int hh = 0; hh < 2; ++hh) {
+                    const v16f sa = row_vec(lds.a_sf(2 * kb + hh) + 32 * i) * sw;
+                    acc[i] = __builtin_elementwise_fma(mfma_f8(fa.h[hh], fb.h[hh], zero), sa, acc[i]);
                 }
             }
-        }
-        if (more) {
-#pragma unroll
-            for (int i = 0; i < C::kMS; ++i) fa[i] = na[i];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) fb[s] = nbf[s];
-        }
-    }
+        });
+    });
+    __syncthreads();                    // every wave is done with the step buffers
 
     // ---- epilogue: BF16 partials, staged so each route row is stored whole ----
+    uint16_t* stage = reinterpret_cast<uint16_t*>(lds.base);  // [BM][BN]
 #pragma unroll
-    for (int i = 0; i < C::kMS; ++i)
+    for (int i = 0; i < MS; ++i) {
+        if (i >= act) break;
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                sm.l2_stage[slice0[i] + acc_row(v)][wn * 64 + s * 32 + c] = bf16_rne(acc[i][s][v]);
+        for (int v = 0; v < 16; ++v)
+            stage[(32 * i + acc_row(v)) * BN + w * 32 + c] = bf16_rne(acc[i][v]);
+    }
     __syncthreads();
-    for (int q = tid; q < BM * 16; q += C::kThreads) {
+    for (int q = threadIdx.x; q < BM * 16; q += NT) {
         const int r = q >> 4, part = q & 15;
         if (r < valid) {
             const int f = a.src[row0 + r];
             if (f >= 0) {
-                const uint4 v = *reinterpret_cast<const uint4*>(&sm.l2_stage[r][part * 8]);
+                const uint4 v = *reinterpret_cast<const uint4*>(stage + r * BN + part * 8);
                 *reinterpret_cast<uint4*>(a.comb + (size_t)f * a.H + nb * BN + part * 8) = v;
             }
         }
     }
 }
 
-template <int BM, int NWM>
-__global__ void __launch_bounds__(NWM * 128)
+// Tile u of a list of `cnt` pool blocks x `nbs` N blocks.  Row-major keeps a
+// pool block's N blocks together; N-major runs each N block across the (at most
+// G) pool blocks of a group, so they share the weight block through L2.
+__device__ __forceinline__ void tile_coords(int u, int cnt, int nbs, int G, bool n_major, int& j,
+                                            int& nb) {
+    if (!n_major) {
+        j = u / nbs;
+        nb = u - j * nbs;
+        return;
+    }
+    const int k = u / (G * nbs);
+    const int within = u - k * G * nbs;
+    const int g = min(G, cnt - k * G);
+    nb = within / g;
+    j = k * G + (within - nb * g);
+}
+
+// Two workgroups per CU (two waves per SIMD) where the registers fit in 256.
+template <int MS>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MS == 1 ? 2 : 1)))
 moe_expert_ffn(MoeArgs a) {
-    __shared__ Smem<BM, NWM> sm;
-    const int total_mb = a.ctrl->total_mb;
-    const int l1_tiles = total_mb * a.nb1;
-    const int total = l1_tiles + total_mb * a.nb2;
+    constexpr int BM = Cfg<MS>::BM;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg<MS>::LDS_BYTES];
+    const Lds<MS> lds{smem};
+    // XCC_ID hardware register, bits [3:0]
+    const int xcd = (__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xf) % a.n_xcd;
+    const int G = a.xcd_group;
+    const int first = a.xcd_info[2 * xcd], cnt = a.xcd_info[2 * xcd + 1];
+    const int l1_tiles = cnt * a.nb1;
+    const int total = l1_tiles + cnt * a.nb2;
     for (;;) {
-        if (threadIdx.x == 0) sm.tile = atomicAdd(&a.ctrl->next_tile, 1);
+        if (threadIdx.x == 0) *lds.tile() = atomicAdd(&a.ctrl->next_tile[xcd], 1);
         __syncthreads();
-        const int u = sm.tile;
+        const int u = *lds.tile();
         __syncthreads();
         if (u >= total) break;
-        int pb, nb;
         const bool is_l1 = u < l1_tiles;
-        if (is_l1) {
-            pb = u / a.nb1;
-            nb = u - pb * a.nb1;
-        } else {
-            const int u2 = u - l1_tiles;
-            if (a.n_major) {
-                // tiles of one expert ordered W2 block by W2 block
-                int lo = 0, hi = a.E - 1;
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (a.mb_start[mid] * a.nb2 <= u2) lo = mid; else hi = mid - 1;
-                }
-                const int mb0 = a.mb_start[lo];
-                const int mbe = a.mb_start[lo + 1] - mb0;
-                const int local = u2 - mb0 * a.nb2;
-                nb = local / mbe;
-                pb = mb0 + (local - nb * mbe);
-            } else {
-                pb = u2 / a.nb2;
-                nb = u2 - pb * a.nb2;
-            }
-        }
+        int j, nb;
+        if (is_l1) tile_coords(u, cnt, a.nb1, G, a.n_major, j, nb);
+        else tile_coords(u - l1_tiles, cnt, a.nb2, G, a.n_major, j, nb);
+        const int pb = a.xcd_pbs[first + j];
         const int e = a.pb_expert[pb];
         const int m_local = pb - a.mb_start[e];
         const int row0 = a.offsets[e] + m_local * BM;
         const int valid = min(BM, a.counts[e] - m_local * BM);
-        if (is_l1) l1_tile<BM, NWM>(a, sm, e, pb, row0, valid, nb);
-        else l2_tile<BM, NWM>(a, sm, e, pb, row0, valid, nb);
+        if (is_l1) l1_tile<MS>(a, lds, e, pb, row0, valid, nb);
+        else l2_tile<MS>(a, lds, e, pb, row0, valid, nb);
         __syncthreads();
     }
 }
 
-template <int BM, int NWM>
+template <int MS>
 static int launch_one(const MoeArgs& a, int num_cus, hipStream_t stream) {
-    using C = TileCfg<BM, NWM>;
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, moe_expert_ffn<BM, NWM>,
-                                                     C::kThreads, 0) != hipSuccess ||
-        per_cu < 1)
-        per_cu = 1;
-    hipLaunchKernelGGL((moe_expert_ffn<BM, NWM>), dim3(num_cus * per_cu), dim3(C::kThreads), 0,
-                       stream, a);
+    static int per_cu = 0;   // occupancy of this instance (same on every call)
+    if (per_cu == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_expert_ffn<MS>, NT, 0) !=
+                hipSuccess || n < 1)
+            n = 1;
+        per_cu = n;
+    }
+    hipLaunchKernelGGL(moe_expert_ffn<MS>, dim3(num_cus * per_cu), dim3(NT), 0, stream, a);
     return num_cus * per_cu;
 }
 
 int launch_expert_ffn(const MoeArgs& a, int num_cus, hipStream_t stream) {
     switch (a.block_m) {
-        case 32: return launch_one<32, 1>(a, num_cus, stream);
-        case 64: return launch_one<64, 2>(a, num_cus, stream);
-        default: return launch_one<128, 2>(a, num_cus, stream);
+        case 32: return launch_one<1>(a, num_cus, stream);
+        case 64: return launch_one<2>(a, num_cus, stream);
+        default: return launch_one<4>(a, num_cus, stream);
     }
 }
 

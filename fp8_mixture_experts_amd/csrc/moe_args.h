@@ -7,12 +7,14 @@
 
 namespace mega_moe {
 
+constexpr int MAX_XCD = 16;
+
 // Control record in device memory, reset by the dispatch scan of every call.
 struct MoeCtrl {
-    int32_t next_tile;   // work queue head of the persistent expert kernel
-    int32_t total_mb;    // number of pool blocks (BLOCK_M rows) over all experts
-    uint32_t error;      // sticky MEGA_MOE_DEVERR_* bits
-    int32_t done_blocks; // reserved
+    int32_t next_tile[MAX_XCD];  // work queue head of each XCD's tiles
+    int32_t total_mb;            // number of pool blocks (BLOCK_M rows) over all experts
+    uint32_t error;              // sticky MEGA_MOE_DEVERR_* bits
+    int32_t pad[2];
 };
 
 struct MoeArgs {
@@ -26,6 +28,8 @@ struct MoeArgs {
     int32_t n_major;    // L2 tile order: 1 = consecutive tiles share a W2 N block
     int32_t num_chunks; // dispatch chunks of DISPATCH_CHUNK routes
     uint32_t wait_spin_limit;  // bound on one L2 tile's wait for its L1 tiles
+    int32_t n_xcd;      // accelerator complex dies (each with its own L2) of the device
+    int32_t xcd_group;  // at most this many pool blocks of one expert form a chunk
 
     // inputs (caller-owned)
     const uint8_t* x;
@@ -54,6 +58,8 @@ struct MoeArgs {
     float* l2_sf;         // [I/64, P_cap]
     uint16_t* comb;       // [R, H]
     uint32_t* ready;      // [PB_cap] finished L1 tiles per pool block
+    int32_t* xcd_pbs;     // [PB_cap] pool blocks of each XCD, XCD after XCD
+    int32_t* xcd_info;    // [2 * MAX_XCD] first entry and count of each XCD's list
     MoeCtrl* ctrl;
 };
 

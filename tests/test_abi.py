@@ -76,7 +76,8 @@ def test_invalid_configs_are_rejected(kw):
     assert B.mega_moe_last_error()
 
 
-@pytest.mark.parametrize("kw", [dict(activation_clamp=10.0), dict(fast_math=1)])
+@pytest.mark.parametrize("kw", [dict(activation_clamp=10.0), dict(fast_math=1),
+                                dict(hidden=8320), dict(intermediate=4224)])
 def test_unbuilt_options_are_unsupported(kw):
     with pytest.raises(B.MegaMoEError) as ei:
         B.mega_moe_plan(_cfg(**kw), 1)
