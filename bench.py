@@ -93,6 +93,9 @@ def main():
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--l2-n-major", type=int, default=-1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many MiB "
+                         "(calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the layer is one GPU's share of expert "
@@ -102,6 +105,7 @@ def main():
     import torch
     from fp8_mixture_experts_amd import binding as B
     from fp8_mixture_experts_amd import synthetic as S
+    from fp8_mixture_experts_amd import rocprof_summary as RS
 
     name = args.workload
     inp = S.make_inputs(name)
@@ -132,6 +136,14 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     prof = B.mega_moe_profile_end(layer.handle, args.steps)
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     status = layer.status()
     if status:
         raise SystemExit(f"device error bits {status:#x}")
@@ -153,7 +165,11 @@ def main():
         roof = {"bound": "hbm", "achieved": work["expert_kernel_bytes"] / (expert_ms / 1e3) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    # calibrated HBM bytes per launch from the committed counter summary of
+    # this workload; None when the library sources changed since it was taken
+    roof["traffic"] = RS.read_traffic(
+        os.path.join(ROOT, "profiles", f"moe_expert_ffn_{name}_hbm_traffic.txt"), name)
+    roof["algorithmic_bytes"] = work["expert_kernel_bytes"]
     roof["kernel"] = f"moe_expert_ffn<{plan.block_m}>"
     roof["kernel_ms"] = expert_ms
     out = {
@@ -169,6 +185,8 @@ def main():
                       "combine": float(k_ms[:, 2].mean())},
         "roofline": roof,
     }
+    if args.copy_probe_mib > 0:
+        out["copy_probe_bytes"] = args.copy_probe_mib << 20
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(name, inp, work)
     print(json.dumps(out), flush=True)

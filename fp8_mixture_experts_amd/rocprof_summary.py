@@ -1,0 +1,163 @@
+"""Turns rocprofv3 result databases into the short text summaries kept under
+``profiles/``.
+
+    python -m fp8_mixture_experts_amd.rocprof_summary trace DB OUT "COMMAND"
+    python -m fp8_mixture_experts_amd.rocprof_summary traffic FETCH_DB WRITE_DB OUT WORKLOAD "COMMAND" COPY_BYTES
+
+``trace`` reads a ``--kernel-trace --stats`` database and writes one line per
+kernel (calls, average and total duration, launch shape, registers, LDS).
+
+``traffic`` reads two ``--pmc`` databases of the same bench command, one with
+``FETCH_SIZE`` and one with ``WRITE_SIZE`` (KiB per dispatch), taken with
+``bench.py --copy-probe-mib N`` so that each run also holds one plain device
+copy of N MiB.  The copy calibrates the counters: a factor per counter equal to
+the bytes the copy is known to read (or write) divided by what the counter
+reported for it.  The expert kernel's calibrated bytes per launch are written
+together with a SHA-256 of the library sources; ``bench.py`` reports them as
+``roofline.traffic`` only while the sources still hash to that value.
+"""
+
+from __future__ import annotations
+
+import glob
+import hashlib
+import os
+import sqlite3
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+EXPERT_KERNEL = "moe_expert_ffn"
+COPY_KERNELS = ("copyBuffer", "copy_kernel", "CopyKernel")
+
+
+def sources_sha256() -> str:
+    """Hash of every library source: a counter reading is stale once it changes."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def _db(path):
+    if os.path.isdir(path):
+        hits = sorted(glob.glob(os.path.join(path, "**", "*_results.db"), recursive=True))
+    else:
+        hits = glob.glob(path)
+    if not hits:
+        raise SystemExit(f"no rocprofv3 database at {path}")
+    return sqlite3.connect(hits[0])
+
+
+def trace(db, out, command):
+    con = _db(db)
+    rows = list(con.execute(
+        "select name, total_calls, total_duration, average, percentage from top_kernels"))
+    info = {r[0]: r[1:] for r in con.execute(
+        "select name, grid_x, workgroup_x, vgpr_count, accum_vgpr_count, lds_size "
+        "from kernels group by name")}
+    lines = ["# rocprofv3 --kernel-trace --stats summary",
+             f"# command: {command}",
+             "# durations in microseconds (the top_kernels view of the database)",
+             f"{'kernel':60s} {'calls':>5s} {'avg_us':>10s} {'total_us':>11s} {'pct':>6s}"
+             "  grid wg vgpr agpr lds"]
+    for name, calls, total, avg, pct in rows:
+        g = info.get(name, ("", "", "", "", ""))
+        lines.append(f"{name[:60]:60s} {calls:5d} {avg:10.2f} {total:11.1f} "
+                     f"{pct:6.2f}  {g[0]} {g[1]} {g[2]} {g[3]} {g[4]}")
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    return text
+
+
+def _counter(con, counter):
+    """Average value of one counter per kernel name, and the dispatch count."""
+    res = {}
+    for name, avg, n in con.execute(
+            "select kernel_name, avg(value), count(distinct dispatch_id) from counters_collection "
+            "where counter_name = ? group by kernel_name", (counter,)):
+        res[name] = (float(avg), int(n))
+    return res
+
+
+def _copy_probe(con, counter):
+    """The copy probe's reading: the largest single copy dispatch in the run."""
+    best = None
+    for name, value in con.execute(
+            "select kernel_name, value from counters_collection where counter_name = ?",
+            (counter,)):
+        if any(k in name for k in COPY_KERNELS) and (best is None or value > best[1]):
+            best = (name, float(value))
+    if best is None:
+        raise SystemExit(f"no copy kernel with {counter} in the run")
+    return best
+
+
+def _pick(res, keys, what):
+    for name, v in res.items():
+        if any(k in name for k in keys):
+            return name, v
+    raise SystemExit(f"no {what} kernel among {sorted(res)}")
+
+
+def traffic(fetch_db, write_db, out, workload, command, copy_bytes):
+    fcon, wcon = _db(fetch_db), _db(write_db)
+    kname, (fetch_kib, nf) = _pick(_counter(fcon, "FETCH_SIZE"), (EXPERT_KERNEL,), "expert")
+    _, (write_kib, nw) = _pick(_counter(wcon, "WRITE_SIZE"), (EXPERT_KERNEL,), "expert")
+    cname, copy_fetch_kib = _copy_probe(fcon, "FETCH_SIZE")
+    _, copy_write_kib = _copy_probe(wcon, "WRITE_SIZE")
+    f_fetch = copy_bytes / (copy_fetch_kib * 1024.0)
+    f_write = copy_bytes / (copy_write_kib * 1024.0)
+    read_b = fetch_kib * 1024.0 * f_fetch
+    write_b = write_kib * 1024.0 * f_write
+    lines = [
+        f"# HBM traffic of {kname} on the {workload} workload (rocprofv3 --pmc, two passes)",
+        f"# command: {command}",
+        f"# calibration kernel: {cname} copying {copy_bytes} bytes",
+        f"copy_fetch_kib: {copy_fetch_kib:.1f}",
+        f"copy_write_kib: {copy_write_kib:.1f}",
+        f"fetch_factor: {f_fetch:.4f}",
+        f"write_factor: {f_write:.4f}",
+        f"expert_fetch_kib_per_launch: {fetch_kib:.1f}   (dispatches: {nf})",
+        f"expert_write_kib_per_launch: {write_kib:.1f}   (dispatches: {nw})",
+        f"read_bytes_per_launch: {read_b:.0f}",
+        f"write_bytes_per_launch: {write_b:.0f}",
+        f"traffic_bytes_per_launch: {read_b + write_b:.0f}",
+        f"workload: {workload}",
+        f"sources_sha256: {sources_sha256()}",
+    ]
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    return text
+
+
+def read_traffic(path, workload):
+    """Calibrated traffic per launch from a summary, or None when it is stale."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.split()[0] if v.split() else ""
+    if kv.get("workload") != workload or kv.get("sources_sha256") != sources_sha256():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def main(argv):
+    if len(argv) >= 4 and argv[0] == "trace":
+        print(trace(argv[1], argv[2], argv[3]), end="")
+    elif len(argv) >= 7 and argv[0] == "traffic":
+        print(traffic(argv[1], argv[2], argv[3], argv[4], argv[5], int(argv[6])), end="")
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
