@@ -52,7 +52,7 @@ struct Layout {
 
 enum {
     L_COUNTS, L_OFFSETS, L_MBSTART, L_PBEXP, L_SLOTMAP, L_SRC, L_CHIST, L_CBASE,
-    L_L1ACTS, L_L1SF, L_L1W, L_L2ACTS, L_L2SF, L_COMB, L_READY, L_XCDPBS, L_XCDINFO, L_CTRL,
+    L_L1ACTS, L_L1SF, L_L1W, L_L2ACTS, L_L2SF, L_COMB, L_READY, L_XCDINFO, L_CTRL,
     L_COUNT
 };
 
@@ -110,7 +110,6 @@ Layout make_layout(const mega_moe_config& c) {
     sz[L_L2SF] = (I / 64) * L.P_cap * 4;
     sz[L_COMB] = L.R_max * H * 2;
     sz[L_READY] = L.PB_cap * 4;
-    sz[L_XCDPBS] = L.PB_cap * 4;
     sz[L_XCDINFO] = 2 * MAX_XCD * 4;
     sz[L_CTRL] = sizeof(MoeCtrl);
     int64_t o = 0;
@@ -252,7 +251,6 @@ int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out) {
     a.l2_sf = (float*)(w + L.off[L_L2SF]);
     a.comb = (uint16_t*)(w + L.off[L_COMB]);
     a.ready = (uint32_t*)(w + L.off[L_READY]);
-    a.xcd_pbs = (int32_t*)(w + L.off[L_XCDPBS]);
     a.xcd_info = (int32_t*)(w + L.off[L_XCDINFO]);
     a.ctrl = (MoeCtrl*)(w + L.off[L_CTRL]);
     h->last_T = 0;

@@ -91,11 +91,16 @@ moe_dispatch_scan(MoeArgs a) {
     // per expert: running sum over chunks (relative chunk bases) and count
     for (int e = tid; e < E; e += SCAN_THREADS) {
         int run = 0;
-        for (int c = 0; c < a.num_chunks; ++c) {
-            const size_t i = (size_t)c * E + e;
-            const int h = a.chunk_hist[i];
-            a.chunk_base[i] = run;
-            run += h;
+        for (int c0 = 0; c0 < a.num_chunks; c0 += 8) {   // 8 loads in flight at a time
+            int h[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                h[j] = c0 + j < a.num_chunks ? a.chunk_hist[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (c0 + j < a.num_chunks) a.chunk_base[(size_t)(c0 + j) * E + e] = run;
+                run += h[j];
+            }
         }
         s_count[e] = run;
         a.counts[e] = run;
@@ -130,47 +135,18 @@ moe_dispatch_scan(MoeArgs a) {
     const size_t ce = (size_t)a.num_chunks * E;
     for (size_t i = tid; i < ce; i += SCAN_THREADS) a.chunk_base[i] += s_off[i % E];
 
-    // padding rows of every segment hold no route
-    for (int ex = 0; ex < E; ++ex) {
-        const int pad0 = s_off[ex] + s_count[ex];
-        const int pad1 = s_off[ex + 1];
-        for (int r = pad0 + tid; r < pad1; r += SCAN_THREADS) a.src[r] = -1;
-    }
+    // every pool row starts as padding; the scatter then claims the routed ones
+    for (int r = tid; r < total_rows; r += SCAN_THREADS) a.src[r] = -1;
 
-    // Per-XCD work lists: each expert's pool blocks are cut into chunks of at
-    // most xcd_group consecutive blocks, and the chunks (expert-major order)
-    // are dealt round-robin to the XCDs.  A chunk stays on one XCD, so its
-    // blocks share the expert's weight stream through that XCD's L2.
-    __shared__ int s_xcd[2 * MAX_XCD];
-    const int G = a.xcd_group;
+    // Per-XCD work: XCD x takes the contiguous pool blocks [x*M/n, (x+1)*M/n)
+    // of the M pool blocks (expert-major), so every XCD gets the same number
+    // of blocks (+-1) and consecutive blocks of one expert mostly share an
+    // XCD and its L2.
     if (tid < a.n_xcd) {
-        int n = 0, chunk = 0;
-        for (int ex = 0; ex < E; ++ex) {
-            const int mb = s_mb[ex + 1] - s_mb[ex];
-            for (int k0 = 0; k0 < mb; k0 += G, ++chunk)
-                if (chunk % a.n_xcd == tid) n += min(G, mb - k0);
-        }
-        s_xcd[MAX_XCD + tid] = n;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int start = 0;
-        for (int x = 0; x < a.n_xcd; ++x) {
-            s_xcd[x] = start;
-            start += s_xcd[MAX_XCD + x];
-        }
-    }
-    __syncthreads();
-    if (tid < a.n_xcd) {
-        int pos = s_xcd[tid], chunk = 0;
-        for (int ex = 0; ex < E; ++ex) {
-            const int mb0 = s_mb[ex], mb = s_mb[ex + 1] - mb0;
-            for (int k0 = 0; k0 < mb; k0 += G, ++chunk)
-                if (chunk % a.n_xcd == tid)
-                    for (int t = k0; t < min(k0 + G, mb); ++t) a.xcd_pbs[pos++] = mb0 + t;
-        }
-        a.xcd_info[2 * tid] = s_xcd[tid];
-        a.xcd_info[2 * tid + 1] = s_xcd[MAX_XCD + tid];
+        const int lo = (int)((int64_t)total_mb * tid / a.n_xcd);
+        const int hi = (int)((int64_t)total_mb * (tid + 1) / a.n_xcd);
+        a.xcd_info[2 * tid] = lo;
+        a.xcd_info[2 * tid + 1] = hi - lo;
     }
 
     // expert of every pool block, and a cleared arrival counter for it

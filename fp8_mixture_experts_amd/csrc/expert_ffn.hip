@@ -8,20 +8,20 @@
 // Work is tiles of BLOCK_M pool rows x 128 output columns: L1 tiles (pool
 // block pb, 128 interleaved W1 rows = 64 outputs = one per-64 scale group) and
 // L2 tiles (pool block pb, 128 columns of H).  The dispatch gives every XCD
-// (accelerator die, each with its own L2) a list of pool blocks, in chunks of
-// at most xcd_group blocks of one expert, and every XCD keeps one queue: first
-// the L1 tiles of its pool blocks, then their L2 tiles.  A workgroup reads its XCD from the
-// XCC_ID hardware register and takes tiles from that queue with one atomic
-// each.  An L2 tile of pb waits until all 2I/128 L1 tiles of pb have published
-// their output through an arrival counter (the role of the L2 arrival mask of
-// 14.3).  Producer and consumer of pb share one XCD and so one L2: the
-// producer waits for its stores to be acknowledged before bumping the counter
-// and the consumer invalidates only its own CU's vector L1 before reading, so
-// no device-wide L2 write-back or invalidation is needed.  L1 tiles never wait
-// and every L2 tile depends only on tiles that precede it in its queue, which
-// running workgroups of the same XCD already own, so the wait always ends,
-// whatever the number of co-resident workgroups; it is still bounded by a spin
-// limit that raises MEGA_MOE_DEVERR_WAIT_TIMEOUT.
+// (accelerator die, each with its own L2) a contiguous range of pool blocks,
+// and every XCD keeps one queue: first the L1 tiles of its pool blocks, then
+// their L2 tiles.  A workgroup reads its XCD from the XCC_ID hardware register
+// and takes tiles from that queue with one atomic each.  An L2 tile of pb
+// waits until all 2I/128 L1 tiles of pb have published their output through
+// an arrival counter (the role of the L2 arrival mask of 14.3).  Producer and
+// consumer of pb share one XCD and so one L2: the producer waits for its
+// stores to be acknowledged before bumping the counter and the consumer
+// invalidates only its own CU's vector L1 before reading, so no device-wide
+// L2 write-back or invalidation is needed.  L1 tiles never wait and every L2
+// tile depends only on tiles that precede it in its queue, which running
+// workgroups of the same XCD already own, so the wait always ends, whatever
+// the number of co-resident workgroups; it is still bounded by a spin limit
+// that raises MEGA_MOE_DEVERR_WAIT_TIMEOUT.
 //
 // Matrix core use (CDNA4).  The FP8 MFMA of gfx950 does not sum its
 // products exactly: within a group of adjacent K it aligns them to the
@@ -36,19 +36,21 @@
 // L2 once per 64-K half (acc += (sa_half*sw) * D_half), as 5.3 and 5.4
 // describe.
 //
-// Memory pipeline.  A workgroup is 4 waves.  Each 128-K step of the tile's
-// operands (BLOCK_M activation rows and 128 weight rows, 128 bytes each) is
-// fetched with fully coalesced 16-byte buffer loads (8 lanes per 128-byte
-// row) into a ring of DEPTH register stages, written to one of two LDS
-// buffers in the MFMA operand layout (XOR-swizzled so both the writes and the
-// fragment reads are free of bank conflicts), and consumed after one
-// workgroup barrier.  Wave w computes output columns [32w, 32w+32) of the
-// tile over all its rows and the whole K step, so no partial sums cross waves.
-// In L1 those 32 stored W1 rows are four interleave groups of 8 (gate, up,
-// gate, up), so the gate and up values of an output sit in lanes c and c+8 of
-// one wave and meet through one swizzle.  The tile's per-row activation scales
-// and per-block weight scales are staged in LDS once per tile; 32-row slices
-// that hold no routes are skipped.
+// Memory pipeline.  A workgroup is 4 waves.  Each 128-K step of a tile is one
+// LDS stage: BLOCK_M activation rows and 128 weight rows of 128 bytes, then
+// the step's per-row activation scales.  Stages are filled by direct
+// global-to-LDS buffer loads (16 bytes per lane, no register staging), S
+// stages deep: at step kb the loads of step kb + S - 1 are issued into the
+// stage that step kb - 1 used, after one wait (this wave's loads of step kb
+// done) and one barrier (every wave's).  Rows are 128 bytes; the 16-byte
+// chunk c of row n sits at position c ^ f(n), f(n) = (n & 7) ^ ((n >> 3) & 1),
+// so each load instruction covers 8 whole rows (fully coalesced) and the MFMA
+// fragment reads (32 rows, one chunk each) hit distinct banks.  Wave w
+// computes output columns [32w, 32w+32) of the tile over all its rows and the
+// whole K step, so no partial sums cross waves.  In L1 those 32 stored W1
+// rows are four interleave groups of 8 (gate, up, gate, up), so the gate and
+// up values of an output sit in lanes c and c+8 of one wave and meet through
+// one swizzle.  32-row slices that hold no routes are skipped.
 #include <hip/hip_runtime.h>
 
 #include "moe_args.h"
@@ -61,12 +63,12 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+#define LDS_AS __attribute__((address_space(3)))
 
 constexpr int BN = 128;              // output columns per tile
 constexpr int BK = 128;              // K bytes per step
 constexpr int NT = 256;              // threads per workgroup (4 waves)
-constexpr int DEPTH = 3;             // register stages of the global-load ring
-constexpr int MAX_SF_GROUPS = 64;    // H/128 and I/64 per tile (H <= 8192, I <= 4096)
+constexpr int MAX_W_SF = 64;         // weight scale blocks per tile (H/128, I/128 <= 64)
 
 __device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c) {
     // scale operands 0 select the plain (unscaled) FP8 x FP8 instruction
@@ -78,39 +80,41 @@ __device__ __forceinline__ v16f mfma_f16(const v8h& a, const v8h& b, const v16f&
 }
 
 // Buffer resource over `bytes` bytes at `base` (gfx9 word 3: raw 32-bit data).
-// Loads whose per-lane offset lies beyond the range return zero.
+// Loads whose per-lane offset lies beyond the range return zero (a direct
+// load to LDS writes zero for those lanes).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+    // every operand here is wave-uniform; say so, so the descriptor lives in SGPRs
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    void* q = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(q, 0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                             0x00020000);
 }
 
-// ---------------------------------------------------------------------------
-// Operand layout.  The MFMA operand of one 32-row (A) or 32-column (B) slice
-// for a 64-K half h: lane L = r + 32g holds row r, K bytes 64h + 32p + 16g +
-// [0,16) for p = 0, 1 (A and B alike, so each MFMA sums exactly the products
-// of its half).  In LDS a step stores, per slice s, half h and part p, one
-// 1 KB block of 64 lanes x 16 bytes; lane L's granule sits at L ^ 2c, where
-// c = 4h + 2p + g is the 16-byte chunk of the row it came from.  The swizzle
-// spreads the coalesced writes (8 chunks of 8 rows) and the fragment reads (64
-// lanes of one block) evenly over the LDS banks.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int lds_granule(int n, int c) {
-    const int s = n >> 5, r = n & 31;
-    const int h = c >> 2, p = (c >> 1) & 1, g = c & 1;
-    return ((s * 2 + h) * 2 + p) * 64 + ((r + 32 * g) ^ (2 * c));
+// 16 bytes per lane from global memory straight into LDS: lane L of the wave
+// writes lds + 16 L (lds must be the same for the whole wave).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)lds, 16, voff, soff, 0, 0);
 }
 
-// Fragment of slice s, half h for this lane from an operand region of LDS.
+// Row swizzle of the stage layout (see the header).
+__device__ __forceinline__ int row_swz(int n) { return (n & 7) ^ ((n >> 3) & 1); }
+
+// ---------------------------------------------------------------------------
+// Operand fragments.  The MFMA operand of one 32-row (A) or 32-column (B)
+// slice for a 64-K half h: lane L = r + 32g holds row r, K bytes 64h + 32p +
+// 16g + [0,16) for p = 0, 1 (A and B alike, so each MFMA sums exactly the
+// products of its half).
+// ---------------------------------------------------------------------------
 __device__ __forceinline__ v8i read_frag(const uint8_t* region, int s, int h) {
     const int L = threadIdx.x & 63;
-    const int g = L >> 5;
-    v4i q[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int c = 4 * h + 2 * p + g;
-        const int gi = ((s * 2 + h) * 2 + p) * 64 + (L ^ (2 * c));
-        q[p] = *reinterpret_cast<const v4i*>(region + gi * 16);
-    }
-    return v8i{q[0][0], q[0][1], q[0][2], q[0][3], q[1][0], q[1][1], q[1][2], q[1][3]};
+    const int r = L & 31, g = L >> 5;
+    const uint8_t* row = region + (32 * s + r) * 128;
+    const int f = row_swz(r);
+    const v4i q0 = *reinterpret_cast<const v4i*>(row + 16 * ((4 * h + g) ^ f));
+    const v4i q1 = *reinterpret_cast<const v4i*>(row + 16 * ((4 * h + 2 + g) ^ f));
+    return v8i{q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
 }
 
 // Both 64-K halves of slice s: dwords 0-7 half 0, dwords 8-15 half 1.
@@ -141,19 +145,6 @@ __device__ __forceinline__ int acc_row(int v) {
     return 8 * (v >> 2) + 4 * ((threadIdx.x >> 5) & 1) + (v & 3);
 }
 
-template <typename T>
-__device__ __forceinline__ void load_row_vec(float (&out)[16], const T* base) {
-    const int g4 = 4 * ((threadIdx.x >> 5) & 1);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const float4 s = *reinterpret_cast<const float4*>(base + 8 * q + g4);
-        out[4 * q + 0] = s.x;
-        out[4 * q + 1] = s.y;
-        out[4 * q + 2] = s.z;
-        out[4 * q + 3] = s.w;
-    }
-}
-
 // Per-row vector in accumulator layout (four float4 runs) as one v16f.
 __device__ __forceinline__ v16f row_vec(const float* base) {
     const int g4 = 4 * ((threadIdx.x >> 5) & 1);
@@ -162,6 +153,39 @@ __device__ __forceinline__ v16f row_vec(const float* base) {
     const float4 c = *reinterpret_cast<const float4*>(base + 16 + g4);
     const float4 d = *reinterpret_cast<const float4*>(base + 24 + g4);
     return v16f{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
+}
+
+// The per-row scales of a step, read from its stage in accumulator layout.
+// The compiler cannot prove these reads disjoint from the direct loads still
+// in flight into the other stages and would wait for all of them; the k
+// loop's wait and barrier already order them, so the reads are issued as
+// inline ds_read_b128 and their completion is awaited by scale_wait, whose
+// operands tie every use of the values to after the wait.
+typedef float v4f __attribute__((ext_vector_type(4)));
+struct ScaleVec {
+    v4f q[4];
+};
+
+__device__ __forceinline__ ScaleVec scale_read(const float* base) {
+    const int g4 = 4 * ((threadIdx.x >> 5) & 1);
+    const uint32_t addr = (uint32_t)(uintptr_t)(LDS_AS const float*)(base + g4);
+    ScaleVec s;
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:32\n\t"
+        "ds_read_b128 %2, %4 offset:64\n\t"
+        "ds_read_b128 %3, %4 offset:96"
+        : "=v"(s.q[0]), "=v"(s.q[1]), "=v"(s.q[2]), "=v"(s.q[3])
+        : "v"(addr)
+        : "memory");
+    return s;
+}
+
+__device__ __forceinline__ v16f scale_wait(ScaleVec& s) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(s.q[0]), "+v"(s.q[1]), "+v"(s.q[2]), "+v"(s.q[3]));
+    return v16f{s.q[0][0], s.q[0][1], s.q[0][2], s.q[0][3], s.q[1][0], s.q[1][1], s.q[1][2],
+                s.q[1][3], s.q[2][0], s.q[2][1], s.q[2][2], s.q[2][3], s.q[3][0], s.q[3][1],
+                s.q[3][2], s.q[3][3]};
 }
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
@@ -194,106 +218,106 @@ __device__ __forceinline__ uint8_t e4m3_code(float v) {
 
 template <int MS>
 struct Cfg {
-    static constexpr int BM = 32 * MS;                     // pool rows per tile
-    static constexpr int A_BYTES = BM * BK;                // A part of one step
-    static constexpr int STEP_BYTES = A_BYTES + BN * BK;   // A + B of one step
-    static constexpr int CHUNKS = STEP_BYTES / 16;
-    static constexpr int PER_THREAD = CHUNKS / NT;         // 16-byte loads per thread per step
-    static_assert(PER_THREAD * NT == CHUNKS && (A_BYTES / 16) == MS * NT, "step split");
-    // LDS map: two step buffers, then scales.  After the K loop the buffers
-    // hold the cross-half reduction and then the epilogue staging.
-    static constexpr int OFF_SF = 2 * STEP_BYTES;
-    static constexpr int SF_BYTES = MAX_SF_GROUPS * BM * 4 + MAX_SF_GROUPS * 4 + BM * 4;
-    static constexpr int LDS_BYTES = OFF_SF + SF_BYTES + 16;
-    static_assert(BM * BN * 4 <= 2 * STEP_BYTES, "reduction buffer");
+    static constexpr int BM = 32 * MS;                    // pool rows per tile
+    static constexpr int A_BYTES = BM * BK;               // activation rows of a stage
+    static constexpr int B_BYTES = BN * BK;               // weight rows of a stage
+    static constexpr int SF_BYTES = 2 * BM * 4;           // per-row scales of a step (2 halves in L2)
+    static constexpr int STAGE = A_BYTES + B_BYTES + SF_BYTES;
+    // stages: one workgroup per CU, so most of the 160 KB of LDS goes to the
+    // load pipeline (two co-resident workgroups gave wrong results, see the
+    // kernel's launch bounds)
+    static constexpr int S = MS == 1 ? 6 : (MS == 2 ? 5 : 4);
+    static constexpr int PT = (BM + BN) / 32;             // 1 KB row blocks per wave per step
+    static constexpr int WAIT = (S - 2) * (PT + 1);       // loads younger than the current step
+    static constexpr int OFF_TILE = S * STAGE;            // per-tile area after the stages
+    static constexpr int LDS_BYTES = OFF_TILE + MAX_W_SF * 4 + BM * 4 + 16;
+    static_assert(WAIT < 64, "vmcnt range");
+    static_assert(BM * BN * 2 <= S * STAGE && 4 * BM * 4 + BM * 64 <= S * STAGE, "epilogue");
 };
 
 template <int MS>
 struct Lds {
     uint8_t* base;
-    __device__ uint8_t* step(int b) const { return base + b * Cfg<MS>::STEP_BYTES; }
-    __device__ float* a_sf(int g) const {
-        return reinterpret_cast<float*>(base + Cfg<MS>::OFF_SF) + g * Cfg<MS>::BM;
-    }
-    __device__ float* w_sf() const {
-        return reinterpret_cast<float*>(base + Cfg<MS>::OFF_SF) + MAX_SF_GROUPS * Cfg<MS>::BM;
-    }
-    __device__ float* row_w() const {   // top-k weight of each row (L1 tiles)
-        return w_sf() + MAX_SF_GROUPS;
-    }
-    __device__ int* tile() const {
-        return reinterpret_cast<int*>(base + Cfg<MS>::OFF_SF + Cfg<MS>::SF_BYTES);
-    }
-    __device__ float* red() const { return reinterpret_cast<float*>(base); }
+    __device__ uint8_t* stage(int i) const { return base + i * Cfg<MS>::STAGE; }
+    __device__ float* w_sf() const { return reinterpret_cast<float*>(base + Cfg<MS>::OFF_TILE); }
+    __device__ float* row_w() const { return w_sf() + MAX_W_SF; }   // top-k weight per row (L1)
+    __device__ int* tile() const { return reinterpret_cast<int*>(row_w() + Cfg<MS>::BM); }
 };
 
-// This thread's share of every step: chunk j < MS belongs to A row
-// tid/8 + 32j, the rest to B row tid/8 + 32(j-MS); chunk column tid%8.
-template <int MS>
+// Issues the direct loads of one step.  Wave w fills the 1 KB row blocks
+// b = 4j + w (rows 8b..8b+7 of the stage: activation rows first, then weight
+// rows): lane q takes row 8b + q/8 and the chunk whose swizzled position is
+// q % 8.  Then each wave loads a quarter of the step's per-row scales (one
+// 64-row group of l1_sf, or the two 64-K halves of l2_sf, in the pool-minor
+// layout).  A step past the end (real = false) still issues the same number
+// of instructions, from lane 0 only, so every wave's count of outstanding
+// loads is the same at every step.
+template <int MS, int HALVES>
 struct Loader {
-    int voff[Cfg<MS>::PER_THREAD];
-    int lds[Cfg<MS>::PER_THREAD];
-    __amdgpu_buffer_rsrc_t ra, rb;
+    static constexpr int PT = Cfg<MS>::PT;
+    static constexpr int Q = HALVES * Cfg<MS>::BM;        // scale bytes per wave (= 4 * rows / 4)
+    __amdgpu_buffer_rsrc_t ra, rb, rs;
+    int voff[PT];
+    int sf_voff;
+    int w;
+    int sf_step;     // bytes between the scale groups of consecutive steps
 
-    __device__ Loader(__amdgpu_buffer_rsrc_t ra_, int a_row_bytes, __amdgpu_buffer_rsrc_t rb_,
-                      int b_row_bytes)
-        : ra(ra_), rb(rb_) {
-        const int t = threadIdx.x;
-        const int c = t & 7;
+    __device__ Loader(__amdgpu_buffer_rsrc_t ra_, __amdgpu_buffer_rsrc_t rb_, int row_bytes,
+                      __amdgpu_buffer_rsrc_t rs_, int P)
+        : ra(ra_), rb(rb_), rs(rs_) {
+        const int lane = threadIdx.x & 63;
+        w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-        for (int j = 0; j < Cfg<MS>::PER_THREAD; ++j) {
-            if (j < MS) {
-                const int n = (t >> 3) + 32 * j;
-                voff[j] = n * a_row_bytes + 16 * c;
-                lds[j] = lds_granule(n, c) * 16;
-            } else {
-                const int n = (t >> 3) + 32 * (j - MS);
-                voff[j] = n * b_row_bytes + 16 * c;
-                lds[j] = Cfg<MS>::A_BYTES + lds_granule(n, c) * 16;
-            }
+        for (int j = 0; j < PT; ++j) {
+            const int n = 8 * (4 * j + w) + (lane >> 3);          // stage row
+            const int r = j < MS ? n : n - Cfg<MS>::BM;         // row of its operand
+            voff[j] = r * row_bytes + 16 * ((lane & 7) ^ row_swz(n));
         }
+        // scale bytes [w*Q, w*Q + Q) of the step's 2*BM*4-byte scale area
+        const int off = w * Q + 16 * lane;
+        const int half = off / (Cfg<MS>::BM * 4);
+        sf_voff = half * P * 4 + (off - half * Cfg<MS>::BM * 4);
+        sf_step = HALVES * P * 4;
     }
-    __device__ __forceinline__ void load(v4i (&r)[Cfg<MS>::PER_THREAD], int kb) const {
+
+    __device__ __forceinline__ void issue(uint8_t* stage, int kb, bool real) const {
+        const int lane = threadIdx.x & 63;
+        const int soff = real ? kb * BK : 0;
 #pragma unroll
-        for (int j = 0; j < Cfg<MS>::PER_THREAD; ++j)
-            r[j] = __builtin_amdgcn_raw_buffer_load_b128(j < MS ? ra : rb, voff[j], kb * BK, 0);
-    }
-    __device__ __forceinline__ void store(uint8_t* step, const v4i (&r)[Cfg<MS>::PER_THREAD]) const {
-#pragma unroll
-        for (int j = 0; j < Cfg<MS>::PER_THREAD; ++j)
-            *reinterpret_cast<v4i*>(step + lds[j]) = r[j];
+        for (int j = 0; j < PT; ++j) {
+            if (real || lane == 0)
+                dma16(j < MS ? ra : rb, stage + (4 * j + w) * 1024, voff[j], soff);
+        }
+        if (lane < Q / 16 && (real || lane == 0))
+            dma16(rs, stage + Cfg<MS>::A_BYTES + Cfg<MS>::B_BYTES + w * Q, sf_voff,
+                  real ? kb * sf_step : 0);
     }
 };
 
-// K loop: DEPTH register stages in flight, two LDS buffers, one barrier per
-// step.  The body has no data-dependent branch, so the compiler waits only
-// for the stage it stores; the last steps re-fetch step KB-1 (cache hits).
-template <int MS, typename Compute>
-__device__ __forceinline__ void k_loop(const Loader<MS>& ld, const Lds<MS>& lds, int KB,
+// Waits for this wave's loads older than the last N, then for every wave.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// K loop over KB steps; compute(stage, kb) reads only stage.
+template <int MS, int HALVES, typename Compute>
+__device__ __forceinline__ void k_loop(const Loader<MS, HALVES>& ld, const Lds<MS>& lds, int KB,
                                        Compute&& compute) {
-    v4i st[DEPTH][Cfg<MS>::PER_THREAD];
+    constexpr int S = Cfg<MS>::S;
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) ld.load(st[d], min(d, KB - 1));
-    int kb = 0;
-    for (; kb + DEPTH <= KB; kb += DEPTH) {
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-            uint8_t* buf = lds.step((kb + d) & 1);
-            ld.store(buf, st[d]);
-            __syncthreads();
-            ld.load(st[d], min(kb + d + DEPTH, KB - 1));
-            compute(buf, kb + d);
-        }
+    for (int d = 0; d < S - 1; ++d) ld.issue(lds.stage(d), d, d < KB);
+    int cur = 0;
+    for (int kb = 0; kb < KB; ++kb) {
+        wait_barrier<Cfg<MS>::WAIT>();
+        const int nk = kb + S - 1;
+        ld.issue(lds.stage(cur == 0 ? S - 1 : cur - 1), nk, nk < KB);
+        compute(lds.stage(cur), kb);
+        cur = cur == S - 1 ? 0 : cur + 1;
     }
-#pragma unroll
-    for (int d = 0; d < DEPTH - 1; ++d) {
-        if (kb + d < KB) {
-            uint8_t* buf = lds.step((kb + d) & 1);
-            ld.store(buf, st[d]);
-            __syncthreads();
-            compute(buf, kb + d);
-        }
-    }
+    // the trailing loads (past the end) land in stages the epilogue reuses
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
 }
 
 template <int N>
@@ -314,19 +338,6 @@ __device__ __forceinline__ void dispatch_act(int act, Fn&& fn) {
     fn(IntTag<1>{});
 }
 
-template <int MS>
-__device__ __forceinline__ void stage_scales(const Lds<MS>& lds, const float* a_base, size_t P,
-                                             int a_groups, const float* w_base, int w_groups,
-                                             int row0) {
-    constexpr int BM = Cfg<MS>::BM;
-    for (int i = threadIdx.x; i < a_groups * BM; i += NT) {
-        const int g = i / BM;
-        const int r = i - g * BM;
-        lds.a_sf(g)[r] = a_base[(size_t)g * P + row0 + r];
-    }
-    for (int i = threadIdx.x; i < w_groups; i += NT) lds.w_sf()[i] = w_base[i];
-}
-
 // ---------------------------------------------------------------------------
 // L1 tile: pool rows [row0, row0 + valid) of expert e, W1 N block nb.
 // ---------------------------------------------------------------------------
@@ -341,12 +352,15 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
     const int c = threadIdx.x & 31;
     const int act = min(MS, (valid + 31) / 32);
 
-    stage_scales(lds, a.l1_sf, P, KB, a.w1_sf + ((size_t)e * a.nb1 + nb) * KB, KB, row0);
+    const float* wsf = a.w1_sf + ((size_t)e * a.nb1 + nb) * KB;
+    for (int i = threadIdx.x; i < KB; i += NT) lds.w_sf()[i] = wsf[i];
     for (int r = threadIdx.x; r < BM; r += NT) lds.row_w()[r] = a.l1_w[row0 + r];
-    const Loader<MS> ld(make_rsrc(a.l1_acts + (size_t)row0 * H, (uint32_t)valid * H), H,
-                        make_rsrc(a.w1 + ((size_t)e * (2 * a.I) + (size_t)nb * BN) * H,
-                                  (uint32_t)BN * H),
-                        H);
+    __syncthreads();
+    const Loader<MS, 1> ld(make_rsrc(a.l1_acts + (size_t)row0 * H, (uint32_t)valid * H),
+                           make_rsrc(a.w1 + ((size_t)e * (2 * a.I) + (size_t)nb * BN) * H,
+                                     (uint32_t)BN * H),
+                           H, make_rsrc(a.l1_sf + row0, (uint32_t)(((KB - 1) * P + BM) * 4)),
+                           (int)P);
 
     v16f acc[MS];
 #pragma unroll
@@ -355,22 +369,24 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
 
     dispatch_act<MS>(act, [&](auto tag) {
         constexpr int ACT = decltype(tag)::value;
-        k_loop<MS>(ld, lds, KB, [&](const uint8_t* buf, int kb) {
+        k_loop<MS, 1>(ld, lds, KB, [&](const uint8_t* stg, int kb) {
             const float sw = lds.w_sf()[kb];
-            const Frag fb = read_frag2(buf + Cfg<MS>::A_BYTES, w);
+            const float* sfa = reinterpret_cast<const float*>(stg + Cfg<MS>::A_BYTES + Cfg<MS>::B_BYTES);
+            const Frag fb = read_frag2(stg + Cfg<MS>::A_BYTES, w);
+            v8h b16[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) b16[q] = f16_part(fb.h[q >> 2], q & 3);
 #pragma unroll
             for (int i = 0; i < ACT; ++i) {
-                const Frag fa = read_frag2(buf, i);
-                v16f d = mfma_f16(f16_part(fa.h[0], 0), f16_part(fb.h[0], 0), zero);
+                const Frag fa = read_frag2(stg, i);
+                ScaleVec sv = scale_read(sfa + 32 * i);
+                v16f d = mfma_f16(f16_part(fa.h[0], 0), b16[0], zero);
 #pragma unroll
-                for (int q = 1; q < 8; ++q)
-                    d = mfma_f16(f16_part(fa.h[q >> 2], q & 3), f16_part(fb.h[q >> 2], q & 3), d);
-                const v16f sa = row_vec(lds.a_sf(kb) + 32 * i) * sw;
-                acc[i] = __builtin_elementwise_fma(d, sa, acc[i]);
+                for (int q = 1; q < 8; ++q) d = mfma_f16(f16_part(fa.h[q >> 2], q & 3), b16[q], d);
+                acc[i] = __builtin_elementwise_fma(d, scale_wait(sv) * sw, acc[i]);
             }
         });
     });
-    __syncthreads();                    // every wave is done with the step buffers
 
     // ---- epilogue: SwiGLU x top-k weight, row amax, FP8 ----
     // Lane c < 8 (mod 16) holds a gate value, lane c + 8 the up value of the
@@ -379,8 +395,9 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
     // the code rule tolerates them); the row amax runs over the wave by DPP
     // and one swizzle, then over the four waves via LDS.  The scale is the
     // exactly rounded amax / 448 the method stores; h / sf is taken as
-    // h * (1 / sf).
-    float* amax = lds.red();                                   // [4][BM]
+    // h * (1 / sf).  Codes go through LDS so every row leaves as 16-byte stores.
+    float* amax = reinterpret_cast<float*>(lds.stage(0));             // [4][BM]
+    uint8_t* codes = lds.stage(0) + 4 * BM * 4;                         // [BM][64]
     const bool gate_lane = (c & 8) == 0;
     float h[MS][16];
 #pragma unroll
@@ -402,7 +419,7 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
         }
     }
     __syncthreads();
-    uint8_t* out = a.l2_acts + (size_t)row0 * a.I + nb * 64 + 16 * w + 8 * ((c >> 4) & 1) + (c & 7);
+    const int col = 16 * w + 8 * ((c >> 4) & 1) + (c & 7);
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
         if (i >= act) break;
@@ -412,11 +429,20 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
             const float am = fmaxf(fmaxf(amax[r], amax[BM + r]), fmaxf(amax[2 * BM + r], amax[3 * BM + r]));
             const float sf = am / 448.0f;
             const float inv = sf > 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
-            if (r < valid) {
-                if (gate_lane) out[(size_t)r * a.I] = e4m3_code(h[i][v] * inv);
-                if (w == 0 && c == 0) a.l2_sf[(size_t)nb * P + row0 + r] = sf;
-            }
+            if (gate_lane) codes[r * 64 + col] = e4m3_code(h[i][v] * inv);
         }
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < BM * 4; q += NT) {
+        const int r = q >> 2, part = q & 3;
+        if (r < valid) {
+            const uint4 v = *reinterpret_cast<const uint4*>(codes + r * 64 + part * 16);
+            *reinterpret_cast<uint4*>(a.l2_acts + (size_t)(row0 + r) * a.I + nb * 64 + part * 16) = v;
+        }
+    }
+    for (int r = threadIdx.x; r < valid; r += NT) {
+        const float am = fmaxf(fmaxf(amax[r], amax[BM + r]), fmaxf(amax[2 * BM + r], amax[3 * BM + r]));
+        a.l2_sf[(size_t)nb * P + row0 + r] = am / 448.0f;
     }
     // publish: the vector L1 writes through, so once every thread's stores are
     // acknowledged they sit in this XCD's L2, where the consumer reads them
@@ -440,6 +466,8 @@ __device__ void l2_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
     const int c = threadIdx.x & 31;
     const int act = min(MS, (valid + 31) / 32);
 
+    const float* wsf = a.w2_sf + ((size_t)e * a.nb2 + nb) * KB;
+    for (int i = threadIdx.x; i < KB; i += NT) lds.w_sf()[i] = wsf[i];
     // wait until every L1 tile of this pool block has published
     if (threadIdx.x == 0) {
         uint32_t spins = 0;
@@ -456,10 +484,10 @@ __device__ void l2_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
     // drop this CU's vector L1 lines so the L1 tiles' output is read from L2
     asm volatile("buffer_inv sc0" ::: "memory");
 
-    stage_scales(lds, a.l2_sf, P, 2 * KB, a.w2_sf + ((size_t)e * a.nb2 + nb) * KB, KB, row0);
-    const Loader<MS> ld(make_rsrc(a.l2_acts + (size_t)row0 * I, (uint32_t)valid * I), I,
-                        make_rsrc(a.w2 + ((size_t)e * a.H + (size_t)nb * BN) * I, (uint32_t)BN * I),
-                        I);
+    const Loader<MS, 2> ld(make_rsrc(a.l2_acts + (size_t)row0 * I, (uint32_t)valid * I),
+                           make_rsrc(a.w2 + ((size_t)e * a.H + (size_t)nb * BN) * I, (uint32_t)BN * I),
+                           I, make_rsrc(a.l2_sf + row0, (uint32_t)(((2 * KB - 1) * P + BM) * 4)),
+                           (int)P);
 
     v16f acc[MS];
 #pragma unroll
@@ -468,24 +496,25 @@ __device__ void l2_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
 
     dispatch_act<MS>(act, [&](auto tag) {
         constexpr int ACT = decltype(tag)::value;
-        k_loop<MS>(ld, lds, KB, [&](const uint8_t* buf, int kb) {
+        k_loop<MS, 2>(ld, lds, KB, [&](const uint8_t* stg, int kb) {
             const float sw = lds.w_sf()[kb];
-            const Frag fb = read_frag2(buf + Cfg<MS>::A_BYTES, w);
+            const float* sfa = reinterpret_cast<const float*>(stg + Cfg<MS>::A_BYTES + Cfg<MS>::B_BYTES);
+            const Frag fb = read_frag2(stg + Cfg<MS>::A_BYTES, w);
 #pragma unroll
             for (int i = 0; i < ACT; ++i) {
-                const Frag fa = read_frag2(buf, i);
+                const Frag fa = read_frag2(stg, i);
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const v16f sa = row_vec(lds.a_sf(2 * kb + hh) + 32 * i) * sw;
-                    acc[i] = __builtin_elementwise_fma(mfma_f8(fa.h[hh], fb.h[hh], zero), sa, acc[i]);
+                    ScaleVec sv = scale_read(sfa + hh * BM + 32 * i);
+                    const v16f d = mfma_f8(fa.h[hh], fb.h[hh], zero);
+                    acc[i] = __builtin_elementwise_fma(d, scale_wait(sv) * sw, acc[i]);
                 }
             }
         });
     });
-    __syncthreads();                    // every wave is done with the step buffers
 
     // ---- epilogue: BF16 partials, staged so each route row is stored whole ----
-    uint16_t* stage = reinterpret_cast<uint16_t*>(lds.base);  // [BM][BN]
+    uint16_t* stage = reinterpret_cast<uint16_t*>(lds.stage(0));  // [BM][BN]
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
         if (i >= act) break;
@@ -506,7 +535,7 @@ __device__ void l2_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
     }
 }
 
-// Tile u of a list of `cnt` pool blocks x `nbs` N blocks.  Row-major keeps a
+// Tile u of a range of `cnt` pool blocks x `nbs` N blocks.  Row-major keeps a
 // pool block's N blocks together; N-major runs each N block across the (at most
 // G) pool blocks of a group, so they share the weight block through L2.
 __device__ __forceinline__ void tile_coords(int u, int cnt, int nbs, int G, bool n_major, int& j,
@@ -523,13 +552,18 @@ __device__ __forceinline__ void tile_coords(int u, int cnt, int nbs, int G, bool
     j = k * G + (within - nb * g);
 }
 
-// Two workgroups per CU (two waves per SIMD) where the registers fit in 256.
+// One workgroup (four waves, one per SIMD) per CU.  Two co-resident
+// workgroups per CU (32- and 64-row tiles with three stages each) produced
+// sporadic wrong tiles on MI355X that no change to the waits, barriers, cache
+// invalidation or LDS layout removed, while the same code at one workgroup
+// per CU is exact; the stage count is sized so that one workgroup fills the
+// LDS and keeps the same bytes in flight.
 template <int MS>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MS == 1 ? 2 : 1)))
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1)))
 moe_expert_ffn(MoeArgs a) {
-    constexpr int BM = Cfg<MS>::BM;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg<MS>::LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg<MS>::LDS_BYTES];
     const Lds<MS> lds{smem};
+    constexpr int BM = Cfg<MS>::BM;
     // XCC_ID hardware register, bits [3:0]
     const int xcd = (__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xf) % a.n_xcd;
     const int G = a.xcd_group;
@@ -539,18 +573,18 @@ moe_expert_ffn(MoeArgs a) {
     for (;;) {
         if (threadIdx.x == 0) *lds.tile() = atomicAdd(&a.ctrl->next_tile[xcd], 1);
         __syncthreads();
-        const int u = *lds.tile();
+        const int u = __builtin_amdgcn_readfirstlane(*lds.tile());
         __syncthreads();
         if (u >= total) break;
         const bool is_l1 = u < l1_tiles;
         int j, nb;
         if (is_l1) tile_coords(u, cnt, a.nb1, G, a.n_major, j, nb);
         else tile_coords(u - l1_tiles, cnt, a.nb2, G, a.n_major, j, nb);
-        const int pb = a.xcd_pbs[first + j];
-        const int e = a.pb_expert[pb];
-        const int m_local = pb - a.mb_start[e];
-        const int row0 = a.offsets[e] + m_local * BM;
-        const int valid = min(BM, a.counts[e] - m_local * BM);
+        const int pb = first + j;
+        const int e = __builtin_amdgcn_readfirstlane(a.pb_expert[pb]);
+        const int m_local = pb - __builtin_amdgcn_readfirstlane(a.mb_start[e]);
+        const int row0 = __builtin_amdgcn_readfirstlane(a.offsets[e]) + m_local * BM;
+        const int valid = min(BM, __builtin_amdgcn_readfirstlane(a.counts[e]) - m_local * BM);
         if (is_l1) l1_tile<MS>(a, lds, e, pb, row0, valid, nb);
         else l2_tile<MS>(a, lds, e, pb, row0, valid, nb);
         __syncthreads();

@@ -29,7 +29,7 @@ struct MoeArgs {
     int32_t num_chunks; // dispatch chunks of DISPATCH_CHUNK routes
     uint32_t wait_spin_limit;  // bound on one L2 tile's wait for its L1 tiles
     int32_t n_xcd;      // accelerator complex dies (each with its own L2) of the device
-    int32_t xcd_group;  // at most this many pool blocks of one expert form a chunk
+    int32_t xcd_group;  // pool blocks per group of the N-major tile order
 
     // inputs (caller-owned)
     const uint8_t* x;
@@ -58,8 +58,7 @@ struct MoeArgs {
     float* l2_sf;         // [I/64, P_cap]
     uint16_t* comb;       // [R, H]
     uint32_t* ready;      // [PB_cap] finished L1 tiles per pool block
-    int32_t* xcd_pbs;     // [PB_cap] pool blocks of each XCD, XCD after XCD
-    int32_t* xcd_info;    // [2 * MAX_XCD] first entry and count of each XCD's list
+    int32_t* xcd_info;    // [2 * MAX_XCD] first pool block and block count of each XCD
     MoeCtrl* ctrl;
 };
 
