@@ -25,7 +25,9 @@ SOURCES = ["dispatch.hip", "expert_ffn.hip", "combine.hip", "api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-result"]
 DEVICE_ONLY = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-               "-mllvm", "-amdgpu-early-inline-all=true"]
+               "-mllvm", "-amdgpu-early-inline-all=true",
+               # MFMA results in VGPRs: the scale promotion reads them right away
+               "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def build(verbose: bool = False) -> str:

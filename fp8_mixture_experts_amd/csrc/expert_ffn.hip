@@ -50,7 +50,7 @@
 // whole K step, so no partial sums cross waves.  In L1 those 32 stored W1
 // rows are four interleave groups of 8 (gate, up, gate, up), so the gate and
 // up values of an output sit in lanes c and c+8 of one wave and meet through
-// one swizzle.  32-row slices that hold no routes are skipped.
+// one DPP move.  32-row slices that hold no routes are skipped.
 #include <hip/hip_runtime.h>
 
 #include "moe_args.h"
@@ -195,25 +195,10 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// Maximum over the 32 lanes that share bit 5 of the lane id: DPP xor-1 and
-// xor-2 within quads, the half-row and row mirrors, then a swizzle xor 16.
+// The value of another lane by a DPP move (CTRL: quad_perm or row_ror).
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ float row_max32(float m) {
-    m = fmaxf(m, dpp_move<0xB1>(m));    // quad_perm [1,0,3,2]
-    m = fmaxf(m, dpp_move<0x4E>(m));    // quad_perm [2,3,0,1]
-    m = fmaxf(m, dpp_move<0x141>(m));   // row_half_mirror
-    m = fmaxf(m, dpp_move<0x140>(m));   // row_mirror
-    return fmaxf(m, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m), 0x401F)));
-}
-
-// OCP E4M3 code of v (|v| <= 448 after the clamp), round to nearest even.
-__device__ __forceinline__ uint8_t e4m3_code(float v) {
-    v = fminf(fmaxf(v, -448.0f), 448.0f);
-    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xff);
 }
 
 template <int MS>
@@ -232,7 +217,7 @@ struct Cfg {
     static constexpr int OFF_TILE = S * STAGE;            // per-tile area after the stages
     static constexpr int LDS_BYTES = OFF_TILE + MAX_W_SF * 4 + BM * 4 + 16;
     static_assert(WAIT < 64, "vmcnt range");
-    static_assert(BM * BN * 2 <= S * STAGE && 4 * BM * 4 + BM * 64 <= S * STAGE, "epilogue");
+    static_assert(BM * BN * 2 <= S * STAGE && BM * 68 * 4 <= S * STAGE, "epilogue buffers");
 };
 
 template <int MS>
@@ -389,60 +374,65 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
     });
 
     // ---- epilogue: SwiGLU x top-k weight, row amax, FP8 ----
-    // Lane c < 8 (mod 16) holds a gate value, lane c + 8 the up value of the
-    // same output, 16w + 8*(c/16) + c%8 of the tile's 64.  silu(g) = g / (1 +
-    // 2^(-g*log2 e)) with the hardware exp2 and reciprocal (a few float32 ulps;
-    // the code rule tolerates them); the row amax runs over the wave by DPP
-    // and one swizzle, then over the four waves via LDS.  The scale is the
-    // exactly rounded amax / 448 the method stores; h / sf is taken as
-    // h * (1 / sf).  Codes go through LDS so every row leaves as 16-byte stores.
-    float* amax = reinterpret_cast<float*>(lds.stage(0));             // [4][BM]
-    uint8_t* codes = lds.stage(0) + 4 * BM * 4;                         // [BM][64]
-    const bool gate_lane = (c & 8) == 0;
-    float h[MS][16];
+    // Lane c < 8 (mod 16)
+    // holds a gate value and lane c + 8 the up value of the same output,
+    // 16w + 8*(c/16) + c%8 of the tile's 64; one DPP rotation within each row
+    // of 16 lanes brings them together.  silu(g) = g / (1 + 2^(-g*log2 e))
+    // with the hardware exp2 and reciprocal (a few float32 ulps; the code rule
+    // tolerates them).  h goes to LDS; then one thread per 16 outputs of a row
+    // takes the row amax over its quad of threads (DPP), the exactly rounded
+    // scale amax / 448, and writes 16 codes (h * (1 / sf)) as one store.
+    constexpr int HS = 68;                                              // h row stride (floats)
+    float* hbuf = reinterpret_cast<float*>(lds.stage(0));              // [BM][HS]
+    {
+        const bool gate_lane = (c & 8) == 0;
+        const int col = 16 * w + 8 * ((c >> 4) & 1) + (c & 7);
 #pragma unroll
-    for (int i = 0; i < MS; ++i) {
-        if (i >= act) break;
-        const v16f wt = row_vec(lds.row_w() + 32 * i);
+        for (int i = 0; i < MS; ++i) {
+            if (i >= act) break;
+            const v16f wt = row_vec(lds.row_w() + 32 * i);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float x = acc[i][v];
-            const float y = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x201F));
-            const float ex = __builtin_amdgcn_exp2f(-x * 1.44269504088896340736f);
-            const float silu = x * __builtin_amdgcn_rcpf(1.0f + ex);
-            h[i][v] = gate_lane ? silu * y * wt[v] : 0.0f;
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float m = row_max32(fabsf(h[i][v]));
-            if (c == 0) amax[w * BM + 32 * i + acc_row(v)] = m;
+            for (int v = 0; v < 16; ++v) {
+                const float x = acc[i][v];
+                const float y = dpp_move<0x128>(x);                     // row_ror:8 = lane c ^ 8
+                const float ex = __builtin_amdgcn_exp2f(-x * 1.44269504088896340736f);
+                const float silu = x * __builtin_amdgcn_rcpf(1.0f + ex);
+                if (gate_lane) hbuf[(32 * i + acc_row(v)) * HS + col] = silu * y * wt[v];
+            }
         }
     }
     __syncthreads();
-    const int col = 16 * w + 8 * ((c >> 4) & 1) + (c & 7);
+    for (int t = threadIdx.x; t < 4 * BM; t += NT) {            // NT is a multiple of 4: quads stay whole
+        const int r = t >> 2, part = t & 3;
+        const float4* src4 = reinterpret_cast<const float4*>(hbuf + r * HS + 16 * part);
+        float hv[16];
 #pragma unroll
-    for (int i = 0; i < MS; ++i) {
-        if (i >= act) break;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = 32 * i + acc_row(v);
-            const float am = fmaxf(fmaxf(amax[r], amax[BM + r]), fmaxf(amax[2 * BM + r], amax[3 * BM + r]));
-            const float sf = am / 448.0f;
-            const float inv = sf > 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
-            if (gate_lane) codes[r * 64 + col] = e4m3_code(h[i][v] * inv);
+        for (int q = 0; q < 4; ++q) {
+            const float4 t = src4[q];
+            hv[4 * q] = t.x; hv[4 * q + 1] = t.y; hv[4 * q + 2] = t.z; hv[4 * q + 3] = t.w;
         }
-    }
-    __syncthreads();
-    for (int q = threadIdx.x; q < BM * 4; q += NT) {
-        const int r = q >> 2, part = q & 3;
+        float m = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) m = fmaxf(m, fabsf(hv[q]));
+        m = fmaxf(m, dpp_move<0xB1>(m));                                // quad_perm [1,0,3,2]
+        m = fmaxf(m, dpp_move<0x4E>(m));                                // quad_perm [2,3,0,1]
+        const float sf = m / 448.0f;
+        const float inv = sf > 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
+        uint32_t code[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float v0 = fminf(fmaxf(hv[4 * q] * inv, -448.0f), 448.0f);
+            float v1 = fminf(fmaxf(hv[4 * q + 1] * inv, -448.0f), 448.0f);
+            float v2 = fminf(fmaxf(hv[4 * q + 2] * inv, -448.0f), 448.0f);
+            float v3 = fminf(fmaxf(hv[4 * q + 3] * inv, -448.0f), 448.0f);
+            int d = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+            code[q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, d, true);
+        }
         if (r < valid) {
-            const uint4 v = *reinterpret_cast<const uint4*>(codes + r * 64 + part * 16);
-            *reinterpret_cast<uint4*>(a.l2_acts + (size_t)(row0 + r) * a.I + nb * 64 + part * 16) = v;
+            *reinterpret_cast<uint4*>(a.l2_acts + (size_t)(row0 + r) * a.I + nb * 64 + part * 16) =
+                uint4{code[0], code[1], code[2], code[3]};
+            if (part == 0) a.l2_sf[(size_t)nb * P + row0 + r] = sf;
         }
-    }
-    for (int r = threadIdx.x; r < valid; r += NT) {
-        const float am = fmaxf(fmaxf(amax[r], amax[BM + r]), fmaxf(amax[2 * BM + r], amax[3 * BM + r]));
-        a.l2_sf[(size_t)nb * P + row0 + r] = am / 448.0f;
     }
     // publish: the vector L1 writes through, so once every thread's stores are
     // acknowledged they sit in this XCD's L2, where the consumer reads them
@@ -552,12 +542,14 @@ __device__ __forceinline__ void tile_coords(int u, int cnt, int nbs, int G, bool
     j = k * G + (within - nb * g);
 }
 
-// One workgroup (four waves, one per SIMD) per CU.  Two co-resident
-// workgroups per CU (32- and 64-row tiles with three stages each) produced
-// sporadic wrong tiles on MI355X that no change to the waits, barriers, cache
-// invalidation or LDS layout removed, while the same code at one workgroup
-// per CU is exact; the stage count is sized so that one workgroup fills the
-// LDS and keeps the same bytes in flight.
+// One workgroup (four waves, one per SIMD) per CU.  Every configuration that
+// put two waves on a SIMD with this direct-to-LDS pipeline (two co-resident
+// four-wave workgroups, or one eight-wave workgroup splitting each step's K
+// halves, with or without the upper waves loading) produced sporadic stale
+// 1 KB blocks in some waves' fragment reads on MI355X; no change to the
+// waits, barriers, extra slack, cache invalidation, out-of-range lanes or LDS
+// layout removed them, while one wave per SIMD is exact.  The stage count is
+// sized so that one workgroup fills the LDS.
 template <int MS>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1)))
 moe_expert_ffn(MoeArgs a) {
