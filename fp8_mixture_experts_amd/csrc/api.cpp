@@ -121,14 +121,18 @@ Layout make_layout(const mega_moe_config& c) {
     return L;
 }
 
+// BLOCK_M tiers by expected routes per expert, as in the SM90 design (13.1),
+// with the thresholds of this kernel on MI355X: a tile streams its weight
+// block once whatever its row count, and 32-row tiles never beat 64-row ones,
+// while 128-row tiles win from about 56 expected routes per expert on.
+constexpr float TIER_64_MAX = 56.5f;
+
 void plan(const mega_moe_config& c, int32_t T, mega_moe_plan_info* p) {
     // expected routes per expert on one GPU (SM90 design 13.1 with one rank)
     const float expected = float(T) * float(c.num_topk) / float(c.num_experts);
     int bm;
     if (c.block_m) bm = c.block_m;
-    else if (expected <= 16.5f) bm = 32;
-    else if (expected <= 64.5f) bm = 64;
-    else bm = 128;
+    else bm = expected <= TIER_64_MAX ? 64 : 128;
     int nm = c.l2_n_major;
     if (nm < 0) nm = expected >= 256.0f ? 1 : 0;   // SM90 design 12.2
     p->expected_tokens_per_expert = expected;

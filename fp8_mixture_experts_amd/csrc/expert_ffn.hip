@@ -15,9 +15,10 @@
 // waits until all 2I/128 L1 tiles of pb have published their output through
 // an arrival counter (the role of the L2 arrival mask of 14.3).  Producer and
 // consumer of pb share one XCD and so one L2: the producer waits for its
-// stores to be acknowledged before bumping the counter and the consumer
-// invalidates only its own CU's vector L1 before reading, so no device-wide
-// L2 write-back or invalidation is needed.  L1 tiles never wait and every L2
+// stores to be acknowledged before bumping the counter and the consumer reads
+// that data with device-scope loads (cache policy SC1, which miss the CU's
+// vector L1 and are served by the XCD's L2), so no L2 write-back or cache
+// invalidation is needed.  L1 tiles never wait and every L2
 // tile depends only on tiles that precede it in its queue, which running
 // workgroups of the same XCD already own, so the wait always ends, whatever
 // the number of co-resident workgroups; it is still bounded by a spin limit
@@ -61,6 +62,7 @@ namespace mega_moe {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
@@ -93,9 +95,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane L of the wave
-// writes lds + 16 L (lds must be the same for the whole wave).
+// writes lds + 16 L (lds must be the same for the whole wave).  AUX is the
+// cache policy; SC1 (device scope) misses the CU's vector L1 and reads the
+// XCD's L2, for data another CU of the XCD wrote in this launch.
+constexpr int SC1 = 16;
+template <int AUX = 0>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voff, int soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)lds, 16, voff, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)lds, 16, voff, soff, 0, AUX);
 }
 
 // Row swizzle of the stage layout (see the header).
@@ -156,36 +162,22 @@ __device__ __forceinline__ v16f row_vec(const float* base) {
 }
 
 // The per-row scales of a step, read from its stage in accumulator layout.
-// The compiler cannot prove these reads disjoint from the direct loads still
-// in flight into the other stages and would wait for all of them; the k
-// loop's wait and barrier already order them, so the reads are issued as
-// inline ds_read_b128 and their completion is awaited by scale_wait, whose
-// operands tie every use of the values to after the wait.
-typedef float v4f __attribute__((ext_vector_type(4)));
-struct ScaleVec {
-    v4f q[4];
-};
-
-__device__ __forceinline__ ScaleVec scale_read(const float* base) {
-    const int g4 = 4 * ((threadIdx.x >> 5) & 1);
-    const uint32_t addr = (uint32_t)(uintptr_t)(LDS_AS const float*)(base + g4);
-    ScaleVec s;
-    asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %4 offset:32\n\t"
-        "ds_read_b128 %2, %4 offset:64\n\t"
-        "ds_read_b128 %3, %4 offset:96"
-        : "=v"(s.q[0]), "=v"(s.q[1]), "=v"(s.q[2]), "=v"(s.q[3])
-        : "v"(addr)
-        : "memory");
-    return s;
-}
-
-__device__ __forceinline__ v16f scale_wait(ScaleVec& s) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(s.q[0]), "+v"(s.q[1]), "+v"(s.q[2]), "+v"(s.q[3]));
-    return v16f{s.q[0][0], s.q[0][1], s.q[0][2], s.q[0][3], s.q[1][0], s.q[1][1], s.q[1][2],
-                s.q[1][3], s.q[2][0], s.q[2][1], s.q[2][2], s.q[2][3], s.q[3][0], s.q[3][1],
-                s.q[3][2], s.q[3][3]};
+// They are read as 16-byte integer vectors, like the operand fragments, and
+// reinterpreted: the compiler treats a float-typed LDS read of the stage as
+// possibly aliasing the direct loads still in flight into the other stages
+// and would drain all of them (vmcnt(0)) before it, while the k loop's wait
+// and barrier already order these reads.  (Issuing them as inline assembly
+// instead is unsafe: the compiler then cannot insert the wait states between
+// an MFMA still reading a register and the LDS read that overwrites it.)
+__device__ __forceinline__ v16f stage_rows(const uint8_t* base) {
+    const int g = 16 * ((threadIdx.x >> 5) & 1);
+    const v4i a = *reinterpret_cast<const v4i*>(base + g);
+    const v4i b = *reinterpret_cast<const v4i*>(base + 32 + g);
+    const v4i c = *reinterpret_cast<const v4i*>(base + 64 + g);
+    const v4i d = *reinterpret_cast<const v4i*>(base + 96 + g);
+    const v16i u = v16i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3],
+                        c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
+    return __builtin_bit_cast(v16f, u);
 }
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
@@ -239,6 +231,8 @@ struct Lds {
 // loads is the same at every step.
 template <int MS, int HALVES>
 struct Loader {
+    // L2 tiles read the activations and scales their L1 tiles just wrote
+    static constexpr int AUX_ACT = HALVES == 2 ? SC1 : 0;
     static constexpr int PT = Cfg<MS>::PT;
     static constexpr int Q = HALVES * Cfg<MS>::BM;        // scale bytes per wave (= 4 * rows / 4)
     __amdgpu_buffer_rsrc_t ra, rb, rs;
@@ -270,11 +264,13 @@ struct Loader {
         const int soff = real ? kb * BK : 0;
 #pragma unroll
         for (int j = 0; j < PT; ++j) {
-            if (real || lane == 0)
-                dma16(j < MS ? ra : rb, stage + (4 * j + w) * 1024, voff[j], soff);
+            if (real || lane == 0) {
+                if (j < MS) dma16<AUX_ACT>(ra, stage + (4 * j + w) * 1024, voff[j], soff);
+                else dma16(rb, stage + (4 * j + w) * 1024, voff[j], soff);
+            }
         }
         if (lane < Q / 16 && (real || lane == 0))
-            dma16(rs, stage + Cfg<MS>::A_BYTES + Cfg<MS>::B_BYTES + w * Q, sf_voff,
+            dma16<AUX_ACT>(rs, stage + Cfg<MS>::A_BYTES + Cfg<MS>::B_BYTES + w * Q, sf_voff,
                   real ? kb * sf_step : 0);
     }
 };
@@ -356,7 +352,7 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
         constexpr int ACT = decltype(tag)::value;
         k_loop<MS, 1>(ld, lds, KB, [&](const uint8_t* stg, int kb) {
             const float sw = lds.w_sf()[kb];
-            const float* sfa = reinterpret_cast<const float*>(stg + Cfg<MS>::A_BYTES + Cfg<MS>::B_BYTES);
+            const uint8_t* sfa = stg + Cfg<MS>::A_BYTES + Cfg<MS>::B_BYTES;
             const Frag fb = read_frag2(stg + Cfg<MS>::A_BYTES, w);
             v8h b16[8];
 #pragma unroll
@@ -364,11 +360,11 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
 #pragma unroll
             for (int i = 0; i < ACT; ++i) {
                 const Frag fa = read_frag2(stg, i);
-                ScaleVec sv = scale_read(sfa + 32 * i);
+                const v16f sv = stage_rows(sfa + 128 * i);
                 v16f d = mfma_f16(f16_part(fa.h[0], 0), b16[0], zero);
 #pragma unroll
                 for (int q = 1; q < 8; ++q) d = mfma_f16(f16_part(fa.h[q >> 2], q & 3), b16[q], d);
-                acc[i] = __builtin_elementwise_fma(d, scale_wait(sv) * sw, acc[i]);
+                acc[i] = __builtin_elementwise_fma(d, sv * sw, acc[i]);
             }
         });
     });
@@ -471,8 +467,6 @@ __device__ void l2_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
         }
     }
     __syncthreads();
-    // drop this CU's vector L1 lines so the L1 tiles' output is read from L2
-    asm volatile("buffer_inv sc0" ::: "memory");
 
     const Loader<MS, 2> ld(make_rsrc(a.l2_acts + (size_t)row0 * I, (uint32_t)valid * I),
                            make_rsrc(a.w2 + ((size_t)e * a.H + (size_t)nb * BN) * I, (uint32_t)BN * I),
@@ -488,16 +482,16 @@ __device__ void l2_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
         constexpr int ACT = decltype(tag)::value;
         k_loop<MS, 2>(ld, lds, KB, [&](const uint8_t* stg, int kb) {
             const float sw = lds.w_sf()[kb];
-            const float* sfa = reinterpret_cast<const float*>(stg + Cfg<MS>::A_BYTES + Cfg<MS>::B_BYTES);
+            const uint8_t* sfa = stg + Cfg<MS>::A_BYTES + Cfg<MS>::B_BYTES;
             const Frag fb = read_frag2(stg + Cfg<MS>::A_BYTES, w);
 #pragma unroll
             for (int i = 0; i < ACT; ++i) {
                 const Frag fa = read_frag2(stg, i);
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    ScaleVec sv = scale_read(sfa + hh * BM + 32 * i);
+                    const v16f sv = stage_rows(sfa + 4 * (hh * BM + 32 * i));
                     const v16f d = mfma_f8(fa.h[hh], fb.h[hh], zero);
-                    acc[i] = __builtin_elementwise_fma(d, scale_wait(sv) * sw, acc[i]);
+                    acc[i] = __builtin_elementwise_fma(d, sv * sw, acc[i]);
                 }
             }
         });
