@@ -124,8 +124,8 @@ Layout make_layout(const mega_moe_config& c) {
 // BLOCK_M tiers by expected routes per expert, as in the SM90 design (13.1),
 // with the thresholds of this kernel on MI355X: a tile streams its weight
 // block once whatever its row count, and 32-row tiles never beat 64-row ones,
-// while 128-row tiles win from about 56 expected routes per expert on.
-constexpr float TIER_64_MAX = 56.5f;
+// while 128-row tiles win from about 50 expected routes per expert on.
+constexpr float TIER_64_MAX = 50.5f;
 
 void plan(const mega_moe_config& c, int32_t T, mega_moe_plan_info* p) {
     // expected routes per expert on one GPU (SM90 design 13.1 with one rank)

@@ -200,15 +200,18 @@ struct Cfg {
     static constexpr int B_BYTES = BN * BK;               // weight rows of a stage
     static constexpr int SF_BYTES = 2 * BM * 4;           // per-row scales of a step (2 halves in L2)
     static constexpr int STAGE = A_BYTES + B_BYTES + SF_BYTES;
-    // stages: one workgroup per CU, so most of the 160 KB of LDS goes to the
-    // load pipeline (two co-resident workgroups gave wrong results, see the
-    // kernel's launch bounds)
-    static constexpr int S = MS == 1 ? 6 : (MS == 2 ? 5 : 4);
+    // Two workgroups share a CU (and each SIMD runs two waves), so each gets
+    // half of the 160 KB of LDS: 3 stages at 32- and 64-row tiles, 2 at
+    // 128-row tiles.  While one workgroup fills or drains its pipeline at a
+    // tile boundary, or waits for an L1 tile, the other keeps loading.
+    static constexpr int WPC = 2;
+    static constexpr int S = MS == 4 ? 2 : 3;
     static constexpr int PT = (BM + BN) / 32;             // 1 KB row blocks per wave per step
     static constexpr int WAIT = (S - 2) * (PT + 1);       // loads younger than the current step
     static constexpr int OFF_TILE = S * STAGE;            // per-tile area after the stages
     static constexpr int LDS_BYTES = OFF_TILE + MAX_W_SF * 4 + BM * 4 + 16;
     static_assert(WAIT < 64, "vmcnt range");
+    static_assert(WPC * LDS_BYTES <= 160 * 1024, "LDS per CU");
     static_assert(BM * BN * 2 <= S * STAGE && BM * 68 * 4 <= S * STAGE, "epilogue buffers");
 };
 
@@ -536,16 +539,11 @@ __device__ __forceinline__ void tile_coords(int u, int cnt, int nbs, int G, bool
     j = k * G + (within - nb * g);
 }
 
-// One workgroup (four waves, one per SIMD) per CU.  Every configuration that
-// put two waves on a SIMD with this direct-to-LDS pipeline (two co-resident
-// four-wave workgroups, or one eight-wave workgroup splitting each step's K
-// halves, with or without the upper waves loading) produced sporadic stale
-// 1 KB blocks in some waves' fragment reads on MI355X; no change to the
-// waits, barriers, extra slack, cache invalidation, out-of-range lanes or LDS
-// layout removed them, while one wave per SIMD is exact.  The stage count is
-// sized so that one workgroup fills the LDS.
+// Two workgroups of four waves per CU, one wave of each per SIMD; the launch
+// puts num_cus * 2 of them in flight and they take tiles until their XCD's
+// queue is empty.
 template <int MS>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Cfg<MS>::WPC)))
 moe_expert_ffn(MoeArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg<MS>::LDS_BYTES];
     const Lds<MS> lds{smem};
