@@ -57,16 +57,31 @@ def work_of(inp):
                 expert_kernel_bytes=w_bytes + R * route_bytes)
 
 
+def _blas_threads():
+    """Threads of the BLAS the oracle's matrix products run on."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d["num_threads"] for d in threadpool_info() if d.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(name, inp, work):
     """Time the oracle on a bounded sample of the workload on this host."""
     from oracle import moe
-    cores = len(os.sched_getaffinity(0))
+    cores = _blas_threads()
     T = inp["x"].shape[0]
     if T <= 128:
-        t0 = time.perf_counter()
-        moe.forward(inp)
-        dt = time.perf_counter() - t0
-        sample = f"full {name} workload ({T} tokens)"
+        # whole forwards, repeated until about 10 s of CPU work
+        reps, t0 = 0, time.perf_counter()
+        while reps < 8 and (reps == 0 or time.perf_counter() - t0 < 10.0):
+            moe.forward(inp)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        sample = f"full {name} workload ({T} tokens), mean of {reps} forwards"
         frac = 1.0
     else:
         n = 64
