@@ -46,12 +46,16 @@
 // done) and one barrier (every wave's).  Rows are 128 bytes; the 16-byte
 // chunk c of row n sits at position c ^ f(n), f(n) = (n & 7) ^ ((n >> 3) & 1),
 // so each load instruction covers 8 whole rows (fully coalesced) and the MFMA
-// fragment reads (32 rows, one chunk each) hit distinct banks.  Wave w
-// computes output columns [32w, 32w+32) of the tile over all its rows and the
-// whole K step, so no partial sums cross waves.  In L1 those 32 stored W1
-// rows are four interleave groups of 8 (gate, up, gate, up), so the gate and
-// up values of an output sit in lanes c and c+8 of one wave and meet through
-// one DPP move.  32-row slices that hold no routes are skipped.
+// fragment reads (32 rows, one chunk each) hit distinct banks.  The tile's
+// 32-row slices x 32-column groups are split over the four waves: at 32- and
+// 64-row tiles wave w computes column group w over all slices, at 128-row
+// tiles each wave computes 2 slices x 2 column groups (a slice's A operand
+// and a group's B operand are then converted and read once for two output
+// blocks).  Each wave sums the whole K step of its blocks, so no partial sums
+// cross waves.  In L1 a column group's 32 stored W1 rows are four interleave
+// groups of 8 (gate, up, gate, up), so the gate and up values of an output
+// sit in lanes c and c+8 of one wave and meet through one DPP move.  32-row
+// slices that hold no routes are skipped.
 #include <hip/hip_runtime.h>
 
 #include "moe_args.h"
@@ -142,6 +146,22 @@ __device__ __forceinline__ v8h f16_part(const v8i& f, int q) {
     const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
     const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
     return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// The same eight FP8 values read straight from the stage (one 8-byte LDS
+// read) and converted: part p of slice (or column group) s, p = 4h + q.
+__device__ __forceinline__ v8h f16_frag_part(const uint8_t* region, int s, int p) {
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    const int L = threadIdx.x & 63;
+    const int r = L & 31, g = L >> 5;
+    const uint8_t* row = region + (32 * s + r) * 128;
+    const int chunk = (4 * (p >> 2) + 2 * ((p & 3) >> 1) + g) ^ row_swz(r);
+    const v2i d = *reinterpret_cast<const v2i*>(row + 16 * chunk + 8 * (p & 1));
+    const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[0], 1.0f, false);
+    const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[0], 1.0f, true);
+    const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[1], 1.0f, false);
+    const v2h e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[1], 1.0f, true);
+    return v8h{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
 }
 
 // Accumulator layout of the 32x32 MFMA: register v of lane l holds row
@@ -304,6 +324,24 @@ __device__ __forceinline__ void k_loop(const Loader<MS, HALVES>& ld, const Lds<M
     __syncthreads();
 }
 
+// Wave layout of a tile with ACT active 32-row slices.  A full 128-row tile
+// is split 2 slices x 2 column groups per wave, so a slice's A operand and a
+// column group's B operand are read and converted once for two output
+// blocks; any other tile gives wave w column group w over all active slices,
+// so no wave idles on a ragged tile.
+template <int MS, int ACT>
+struct Lay {
+    static constexpr bool GRID = MS == 4 && ACT == 4;
+    static constexpr int NJ = GRID ? 2 : ACT;     // 32-row slices per wave
+    static constexpr int NG = GRID ? 2 : 1;       // 32-column groups per wave
+    int s0, g0;
+    __device__ Lay() {
+        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        s0 = GRID ? 2 * (w >> 1) : 0;
+        g0 = GRID ? 2 * (w & 1) : w;
+    }
+};
+
 template <int N>
 struct IntTag {
     static constexpr int value = N;
@@ -332,7 +370,6 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
     const int H = a.H;
     const int KB = H / BK;
     const size_t P = a.P_cap;
-    const int w = threadIdx.x >> 6;
     const int c = threadIdx.x & 31;
     const int act = min(MS, (valid + 31) / 32);
 
@@ -346,60 +383,98 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
                            H, make_rsrc(a.l1_sf + row0, (uint32_t)(((KB - 1) * P + BM) * 4)),
                            (int)P);
 
-    v16f acc[MS];
-#pragma unroll
-    for (int i = 0; i < MS; ++i) acc[i] = v16f{};
     const v16f zero = v16f{};
+    // ---- epilogue buffer: h of the tile, written from the accumulators ----
+    // Lane c < 8 (mod 16) of a column group holds a gate value and lane c + 8
+    // the up value of the same output, 16g + 8*(c/16) + c%8 of the tile's 64
+    // for column group g; one DPP rotation within each row of 16 lanes brings
+    // them together.  silu(g) = g / (1 + 2^(-g*log2 e)) with the hardware exp2
+    // and reciprocal (a few float32 ulps; the code rule tolerates them).  h
+    // goes to LDS; then one thread per 16 outputs of a row takes the row amax
+    // over its quad of threads (DPP), the exactly rounded scale amax / 448,
+    // and writes 16 codes (h * (1 / sf)) as one store.
+    constexpr int HS = 68;                                              // h row stride (floats)
+    float* hbuf = reinterpret_cast<float*>(lds.stage(0));              // [BM][HS]
 
     dispatch_act<MS>(act, [&](auto tag) {
         constexpr int ACT = decltype(tag)::value;
+        using LY = Lay<MS, ACT>;
+        const LY ly;
+        v16f acc[LY::NJ][LY::NG];
+#pragma unroll
+        for (int j = 0; j < LY::NJ; ++j)
+#pragma unroll
+            for (int q = 0; q < LY::NG; ++q) acc[j][q] = v16f{};
+
         k_loop<MS, 1>(ld, lds, KB, [&](const uint8_t* stg, int kb) {
             const float sw = lds.w_sf()[kb];
             const uint8_t* sfa = stg + Cfg<MS>::A_BYTES + Cfg<MS>::B_BYTES;
-            const Frag fb = read_frag2(stg + Cfg<MS>::A_BYTES, w);
-            v8h b16[8];
+            if constexpr (LY::GRID) {
+                // eight 16-K parts; per part the B operands of the two column
+                // groups and the A operand of each slice are read and
+                // converted once and feed four independent MFMA chains
+                v16f d[LY::NJ][LY::NG];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) b16[q] = f16_part(fb.h[q >> 2], q & 3);
+                for (int p = 0; p < 8; ++p) {
+                    v8h b16[LY::NG];
 #pragma unroll
-            for (int i = 0; i < ACT; ++i) {
-                const Frag fa = read_frag2(stg, i);
-                const v16f sv = stage_rows(sfa + 128 * i);
-                v16f d = mfma_f16(f16_part(fa.h[0], 0), b16[0], zero);
+                    for (int q = 0; q < LY::NG; ++q)
+                        b16[q] = f16_frag_part(stg + Cfg<MS>::A_BYTES, ly.g0 + q, p);
 #pragma unroll
-                for (int q = 1; q < 8; ++q) d = mfma_f16(f16_part(fa.h[q >> 2], q & 3), b16[q], d);
-                acc[i] = __builtin_elementwise_fma(d, sv * sw, acc[i]);
+                    for (int j = 0; j < LY::NJ; ++j) {
+                        const v8h a16 = f16_frag_part(stg, ly.s0 + j, p);
+#pragma unroll
+                        for (int q = 0; q < LY::NG; ++q)
+                            d[j][q] = mfma_f16(a16, b16[q], p == 0 ? zero : d[j][q]);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < LY::NJ; ++j) {
+                    const v16f svw = stage_rows(sfa + 128 * (ly.s0 + j)) * sw;
+#pragma unroll
+                    for (int q = 0; q < LY::NG; ++q)
+                        acc[j][q] = __builtin_elementwise_fma(d[j][q], svw, acc[j][q]);
+                }
+            } else {
+                // one column group: its B operand converted once per step,
+                // then one MFMA chain per active slice
+                const Frag fb = read_frag2(stg + Cfg<MS>::A_BYTES, ly.g0);
+                v8h b16[8];
+#pragma unroll
+                for (int p = 0; p < 8; ++p) b16[p] = f16_part(fb.h[p >> 2], p & 3);
+#pragma unroll
+                for (int j = 0; j < LY::NJ; ++j) {
+                    const Frag fa = read_frag2(stg, j);
+                    const v16f sv = stage_rows(sfa + 128 * j);
+                    v16f d = mfma_f16(f16_part(fa.h[0], 0), b16[0], zero);
+#pragma unroll
+                    for (int p = 1; p < 8; ++p) d = mfma_f16(f16_part(fa.h[p >> 2], p & 3), b16[p], d);
+                    acc[j][0] = __builtin_elementwise_fma(d, sv * sw, acc[j][0]);
+                }
             }
         });
-    });
 
-    // ---- epilogue: SwiGLU x top-k weight, row amax, FP8 ----
-    // Lane c < 8 (mod 16)
-    // holds a gate value and lane c + 8 the up value of the same output,
-    // 16w + 8*(c/16) + c%8 of the tile's 64; one DPP rotation within each row
-    // of 16 lanes brings them together.  silu(g) = g / (1 + 2^(-g*log2 e))
-    // with the hardware exp2 and reciprocal (a few float32 ulps; the code rule
-    // tolerates them).  h goes to LDS; then one thread per 16 outputs of a row
-    // takes the row amax over its quad of threads (DPP), the exactly rounded
-    // scale amax / 448, and writes 16 codes (h * (1 / sf)) as one store.
-    constexpr int HS = 68;                                              // h row stride (floats)
-    float* hbuf = reinterpret_cast<float*>(lds.stage(0));              // [BM][HS]
-    {
+        // the k loop ended with a barrier, so the stages are free for h
         const bool gate_lane = (c & 8) == 0;
-        const int col = 16 * w + 8 * ((c >> 4) & 1) + (c & 7);
 #pragma unroll
-        for (int i = 0; i < MS; ++i) {
-            if (i >= act) break;
-            const v16f wt = row_vec(lds.row_w() + 32 * i);
+        for (int j = 0; j < LY::NJ; ++j) {
+            const int sl = ly.s0 + j;
+            const v16f wt = row_vec(lds.row_w() + 32 * sl);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float x = acc[i][v];
-                const float y = dpp_move<0x128>(x);                     // row_ror:8 = lane c ^ 8
-                const float ex = __builtin_amdgcn_exp2f(-x * 1.44269504088896340736f);
-                const float silu = x * __builtin_amdgcn_rcpf(1.0f + ex);
-                if (gate_lane) hbuf[(32 * i + acc_row(v)) * HS + col] = silu * y * wt[v];
+            for (int q = 0; q < LY::NG; ++q) {
+                const int col = 16 * (ly.g0 + q) + 8 * ((c >> 4) & 1) + (c & 7);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float x = acc[j][q][v];
+                    const float y = dpp_move<0x128>(x);                 // row_ror:8 = lane c ^ 8
+                    const float ex = __builtin_amdgcn_exp2f(-x * 1.44269504088896340736f);
+                    const float silu = x * __builtin_amdgcn_rcpf(1.0f + ex);
+                    if (gate_lane) hbuf[(32 * sl + acc_row(v)) * HS + col] = silu * y * wt[v];
+                }
             }
         }
-    }
+    });
+
     __syncthreads();
     for (int t = threadIdx.x; t < 4 * BM; t += NT) {            // NT is a multiple of 4: quads stay whole
         const int r = t >> 2, part = t & 3;
@@ -451,7 +526,6 @@ __device__ void l2_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
     const int I = a.I;
     const int KB = I / BK;
     const size_t P = a.P_cap;
-    const int w = threadIdx.x >> 6;
     const int c = threadIdx.x & 31;
     const int act = min(MS, (valid + 31) / 32);
 
@@ -476,39 +550,51 @@ __device__ void l2_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
                            I, make_rsrc(a.l2_sf + row0, (uint32_t)(((2 * KB - 1) * P + BM) * 4)),
                            (int)P);
 
-    v16f acc[MS];
-#pragma unroll
-    for (int i = 0; i < MS; ++i) acc[i] = v16f{};
     const v16f zero = v16f{};
+    uint16_t* stage = reinterpret_cast<uint16_t*>(lds.stage(0));  // BF16 [BM][BN] after the k loop
 
     dispatch_act<MS>(act, [&](auto tag) {
         constexpr int ACT = decltype(tag)::value;
+        using LY = Lay<MS, ACT>;
+        const LY ly;
+        v16f acc[LY::NJ][LY::NG];
+#pragma unroll
+        for (int j = 0; j < LY::NJ; ++j)
+#pragma unroll
+            for (int q = 0; q < LY::NG; ++q) acc[j][q] = v16f{};
+
         k_loop<MS, 2>(ld, lds, KB, [&](const uint8_t* stg, int kb) {
             const float sw = lds.w_sf()[kb];
             const uint8_t* sfa = stg + Cfg<MS>::A_BYTES + Cfg<MS>::B_BYTES;
-            const Frag fb = read_frag2(stg + Cfg<MS>::A_BYTES, w);
+            Frag fb[LY::NG];
 #pragma unroll
-            for (int i = 0; i < ACT; ++i) {
-                const Frag fa = read_frag2(stg, i);
+            for (int q = 0; q < LY::NG; ++q) fb[q] = read_frag2(stg + Cfg<MS>::A_BYTES, ly.g0 + q);
+#pragma unroll
+            for (int j = 0; j < LY::NJ; ++j) {
+                const int sl = ly.s0 + j;
+                const Frag fa = read_frag2(stg, sl);
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const v16f sv = stage_rows(sfa + 4 * (hh * BM + 32 * i));
-                    const v16f d = mfma_f8(fa.h[hh], fb.h[hh], zero);
-                    acc[i] = __builtin_elementwise_fma(d, sv * sw, acc[i]);
+                    const v16f svw = stage_rows(sfa + 4 * (hh * BM + 32 * sl)) * sw;
+#pragma unroll
+                    for (int q = 0; q < LY::NG; ++q) {
+                        const v16f d = mfma_f8(fa.h[hh], fb[q].h[hh], zero);
+                        acc[j][q] = __builtin_elementwise_fma(d, svw, acc[j][q]);
+                    }
                 }
             }
         });
-    });
 
-    // ---- epilogue: BF16 partials, staged so each route row is stored whole ----
-    uint16_t* stage = reinterpret_cast<uint16_t*>(lds.stage(0));  // [BM][BN]
+        // ---- epilogue: BF16 partials, staged so each route row is stored whole ----
 #pragma unroll
-    for (int i = 0; i < MS; ++i) {
-        if (i >= act) break;
+        for (int j = 0; j < LY::NJ; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            stage[(32 * i + acc_row(v)) * BN + w * 32 + c] = bf16_rne(acc[i][v]);
-    }
+            for (int q = 0; q < LY::NG; ++q)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    stage[(32 * (ly.s0 + j) + acc_row(v)) * BN + 32 * (ly.g0 + q) + c] =
+                        bf16_rne(acc[j][q][v]);
+    });
     __syncthreads();
     for (int q = threadIdx.x; q < BM * 16; q += NT) {
         const int r = q >> 4, part = q & 15;
