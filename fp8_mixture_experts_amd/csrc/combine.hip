@@ -35,15 +35,33 @@ moe_combine(MoeArgs a) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < a.k; ++j) {
-        const int e = a.topk_idx[(size_t)t * a.k + j];
-        if (e < 0 || e >= a.E) continue;
-        const uint4 p = *reinterpret_cast<const uint4*>(a.comb + ((size_t)t * a.k + j) * a.H + col);
-        const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+    // slots in groups of 8: all expert ids of the group, then all active
+    // partial loads in flight together, then the adds in slot order.  An
+    // inactive slot contributes +0, which leaves the sum unchanged: it starts
+    // at +0, so it is never -0.
+    const int* idx = a.topk_idx + (size_t)t * a.k;
+    const uint16_t* part = a.comb + (size_t)t * a.k * a.H + col;
+    for (int j0 = 0; j0 < a.k; j0 += 8) {
+        const int n = min(8, a.k - j0);
+        uint4 p[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] += __uint_as_float(w[i] << 16);
-            acc[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
+        for (int j = 0; j < 8; ++j) {
+            p[j] = uint4{0u, 0u, 0u, 0u};
+            if (j < n) {
+                const int e = idx[j0 + j];
+                if (e >= 0 && e < a.E)
+                    p[j] = *reinterpret_cast<const uint4*>(part + (size_t)(j0 + j) * a.H);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j >= n) break;
+            const uint32_t w[4] = {p[j].x, p[j].y, p[j].z, p[j].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] += __uint_as_float(w[i] << 16);
+                acc[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
+            }
         }
     }
     uint4 o;

@@ -3,7 +3,11 @@
 // each routed token into its expert's pool ("MegaMoE SM90 Implementation
 // Design (Final)" 3.3 phase 1 and 9.2; one GPU, so every source is local).
 //
-// Four launches, all on the caller's stream:
+// Up to 4096 routes: two launches on the caller's stream,
+//   moe_dispatch_small   one workgroup: histogram, scan, stable ranks, slot
+//                        map and source metadata, resets
+//   moe_dispatch_gather  (below);
+// larger batches: four,
 //   moe_dispatch_count   one workgroup per chunk of 1024 routes: histogram
 //   moe_dispatch_scan    one workgroup: per-expert scan over chunks, the
 //                        wavefront prefix scan over experts (offsets, pool
@@ -79,35 +83,16 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
     return out;
 }
 
-__global__ void __launch_bounds__(SCAN_THREADS)
-moe_dispatch_scan(MoeArgs a) {
-    __shared__ int s_count[MAX_EXPERTS];
-    __shared__ int s_off[MAX_EXPERTS + 1];
-    __shared__ int s_mb[MAX_EXPERTS + 1];
-    __shared__ int s_wave[SCAN_THREADS / 64 + 1];
+// With every expert's count in s_count (one workgroup of SCAN_THREADS):
+// 128-aligned segment offsets and pool blocks by a wavefront prefix scan over
+// the experts, the expert of every pool block with a cleared arrival counter,
+// each XCD's range of pool blocks, the cleared queue heads, and -1 in `src`
+// for the padding rows of every segment (the routed rows are written by the
+// ranking).  Leaves the segment offsets in s_off.
+__device__ void finish_counts(const MoeArgs& a, const int* s_count, int* s_off, int* s_mb,
+                              int* s_wave) {
     const int tid = threadIdx.x;
     const int E = a.E;
-
-    // per expert: running sum over chunks (relative chunk bases) and count
-    for (int e = tid; e < E; e += SCAN_THREADS) {
-        int run = 0;
-        for (int c0 = 0; c0 < a.num_chunks; c0 += 8) {   // 8 loads in flight at a time
-            int h[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                h[j] = c0 + j < a.num_chunks ? a.chunk_hist[(size_t)(c0 + j) * E + e] : 0;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (c0 + j < a.num_chunks) a.chunk_base[(size_t)(c0 + j) * E + e] = run;
-                run += h[j];
-            }
-        }
-        s_count[e] = run;
-        a.counts[e] = run;
-    }
-    __syncthreads();
-
-    // prefix scan over experts (E <= SCAN_THREADS): padded segments, pool blocks
     const int e = tid;
     const int cnt = e < E ? s_count[e] : 0;
     const int padded = (cnt + POOL_ALIGN - 1) / POOL_ALIGN * POOL_ALIGN;
@@ -118,6 +103,7 @@ moe_dispatch_scan(MoeArgs a) {
     if (e < E) {
         s_off[e] = off;
         s_mb[e] = mb0;
+        a.counts[e] = cnt;
         a.offsets[e] = off;
         a.mb_start[e] = mb0;
     }
@@ -131,12 +117,13 @@ moe_dispatch_scan(MoeArgs a) {
     }
     __syncthreads();
 
-    // absolute chunk bases
-    const size_t ce = (size_t)a.num_chunks * E;
-    for (size_t i = tid; i < ce; i += SCAN_THREADS) a.chunk_base[i] += s_off[i % E];
-
-    // every pool row starts as padding; the scatter then claims the routed ones
-    for (int r = tid; r < total_rows; r += SCAN_THREADS) a.src[r] = -1;
+    // padding rows of each segment: [off + count, off + align128(count))
+    for (int i = tid; i < E * POOL_ALIGN; i += SCAN_THREADS) {
+        const int ex = i / POOL_ALIGN, r = i - ex * POOL_ALIGN;
+        const int c = s_count[ex];
+        const int pad = (c + POOL_ALIGN - 1) / POOL_ALIGN * POOL_ALIGN - c;
+        if (r < pad) a.src[s_off[ex] + c + r] = -1;
+    }
 
     // Per-XCD work: XCD x takes the contiguous pool blocks [x*M/n, (x+1)*M/n)
     // of the M pool blocks (expert-major), so every XCD gets the same number
@@ -161,6 +148,117 @@ moe_dispatch_scan(MoeArgs a) {
     }
 }
 
+__global__ void __launch_bounds__(SCAN_THREADS)
+moe_dispatch_scan(MoeArgs a) {
+    __shared__ int s_count[MAX_EXPERTS];
+    __shared__ int s_off[MAX_EXPERTS + 1];
+    __shared__ int s_mb[MAX_EXPERTS + 1];
+    __shared__ int s_wave[SCAN_THREADS / 64 + 1];
+    const int tid = threadIdx.x;
+    const int E = a.E;
+
+    // per expert: running sum over chunks (relative chunk bases) and count
+    for (int e = tid; e < E; e += SCAN_THREADS) {
+        int run = 0;
+        for (int c0 = 0; c0 < a.num_chunks; c0 += 8) {   // 8 loads in flight at a time
+            int h[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                h[j] = c0 + j < a.num_chunks ? a.chunk_hist[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (c0 + j < a.num_chunks) a.chunk_base[(size_t)(c0 + j) * E + e] = run;
+                run += h[j];
+            }
+        }
+        s_count[e] = run;
+    }
+    __syncthreads();
+    finish_counts(a, s_count, s_off, s_mb, s_wave);
+
+    // absolute chunk bases
+    const size_t ce = (size_t)a.num_chunks * E;
+    for (size_t i = tid; i < ce; i += SCAN_THREADS) a.chunk_base[i] += s_off[i % E];
+}
+
+// Stable rank of route f among the lanes of its wave with the same key, and
+// the number of such lanes (keys 0..E, E = not routed), by ballots bit by bit.
+__device__ __forceinline__ int wave_rank(int key, int key_bits, int* peers_count) {
+    const int lane = lane_id();
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint64_t peers = __ballot(1);
+    for (int b = 0; b < key_bits; ++b) {
+        const bool bit = (key >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    *peers_count = __popcll(peers);
+    return __popcll(peers & lt_mask);
+}
+
+// Small batches (at most SMALL_CHUNKS chunks of routes; each ranking round
+// costs about as much as a launch, so larger batches take the multi-workgroup
+// path): the whole dispatch but the pool copy in one workgroup: LDS
+// histogram, the scan above, then
+// stable ranks in rounds of SCAN_THREADS routes (ballots inside a wave, per
+// wave counts in LDS across waves, a running base per expert across rounds).
+constexpr int SMALL_CHUNKS = 4;
+constexpr int SMALL_WAVES = SCAN_THREADS / 64;
+
+__global__ void __launch_bounds__(SCAN_THREADS)
+moe_dispatch_small(MoeArgs a) {
+    __shared__ int s_count[MAX_EXPERTS];
+    __shared__ int s_off[MAX_EXPERTS + 1];
+    __shared__ int s_mb[MAX_EXPERTS + 1];
+    __shared__ int s_wave[SCAN_THREADS / 64 + 1];
+    __shared__ int wcnt[SMALL_WAVES][MAX_EXPERTS];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int E = a.E;
+
+    for (int e = tid; e < E; e += SCAN_THREADS) s_count[e] = 0;
+    __syncthreads();
+    bool bad = false;
+    for (int f = tid; f < a.R; f += SCAN_THREADS) {
+        const int e = a.topk_idx[f];
+        if (e >= 0 && e < E) atomicAdd(&s_count[e], 1);
+        else if (e >= E) bad = true;
+    }
+    if (bad) atomicOr(&a.ctrl->error, MEGA_MOE_DEVERR_BAD_EXPERT);
+    __syncthreads();
+    finish_counts(a, s_count, s_off, s_mb, s_wave);
+
+    int key_bits = 0;
+    while ((1 << key_bits) <= E) ++key_bits;
+    // s_off becomes the running base of each expert's next slot
+    for (int round = 0; round * SCAN_THREADS < a.R; ++round) {
+        for (int i = tid; i < SMALL_WAVES * E; i += SCAN_THREADS) wcnt[i / E][i % E] = 0;
+        __syncthreads();
+        const int f = round * SCAN_THREADS + tid;
+        const int e = f < a.R ? a.topk_idx[f] : -1;
+        const bool valid = e >= 0 && e < E;
+        int n_same;
+        const int rank = wave_rank(valid ? e : E, key_bits, &n_same);
+        if (valid && rank == 0) wcnt[wave][e] = n_same;
+        __syncthreads();
+        if (valid) {
+            int slot = s_off[e] + rank;
+            for (int w = 0; w < wave; ++w) slot += wcnt[w][e];
+            a.slot_map[f] = slot;
+            a.src[slot] = f;
+        } else if (f < a.R) {
+            a.slot_map[f] = -1;
+        }
+        __syncthreads();
+        for (int ex = tid; ex < E; ex += SCAN_THREADS) {
+            int sum = 0;
+            for (int w = 0; w < SMALL_WAVES; ++w) sum += wcnt[w][ex];
+            s_off[ex] += sum;
+        }
+        __syncthreads();
+    }
+}
+
 __global__ void __launch_bounds__(DISPATCH_THREADS)
 moe_dispatch_scatter(MoeArgs a) {
     constexpr int NW = DISPATCH_THREADS / 64;
@@ -175,7 +273,6 @@ moe_dispatch_scatter(MoeArgs a) {
     while ((1 << key_bits) <= E) ++key_bits;   // keys 0..E (E = "no expert")
 
     for (int e = tid; e < E; e += DISPATCH_THREADS) running[e] = 0;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
     for (int round = 0; round < DISPATCH_CHUNK / DISPATCH_THREADS; ++round) {
         for (int i = tid; i < NW * E; i += DISPATCH_THREADS) wcnt[i / E][i % E] = 0;
@@ -183,16 +280,9 @@ moe_dispatch_scatter(MoeArgs a) {
         const int f = c * DISPATCH_CHUNK + round * DISPATCH_THREADS + tid;
         int e = f < a.R ? a.topk_idx[f] : -1;
         const bool valid = e >= 0 && e < E;
-        const int key = valid ? e : E;
-        // lanes of this wave with the same key (a match by ballots, bit by bit)
-        uint64_t peers = __ballot(1);
-        for (int b = 0; b < key_bits; ++b) {
-            const bool bit = (key >> b) & 1;
-            const uint64_t m = __ballot(bit);
-            peers &= bit ? m : ~m;
-        }
-        const int rank = __popcll(peers & lt_mask);
-        if (valid && rank == 0) wcnt[wave][e] = __popcll(peers);
+        int n_same;
+        const int rank = wave_rank(valid ? e : E, key_bits, &n_same);
+        if (valid && rank == 0) wcnt[wave][e] = n_same;
         __syncthreads();
         if (valid) {
             int before = running[e] + rank;
@@ -232,9 +322,13 @@ moe_dispatch_gather(MoeArgs a) {
 }
 
 void launch_dispatch(const MoeArgs& a, int gather_blocks, hipStream_t stream) {
-    hipLaunchKernelGGL(moe_dispatch_count, dim3(a.num_chunks), dim3(DISPATCH_THREADS), 0, stream, a);
-    hipLaunchKernelGGL(moe_dispatch_scan, dim3(1), dim3(SCAN_THREADS), 0, stream, a);
-    hipLaunchKernelGGL(moe_dispatch_scatter, dim3(a.num_chunks), dim3(DISPATCH_THREADS), 0, stream, a);
+    if (a.num_chunks <= SMALL_CHUNKS) {
+        hipLaunchKernelGGL(moe_dispatch_small, dim3(1), dim3(SCAN_THREADS), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL(moe_dispatch_count, dim3(a.num_chunks), dim3(DISPATCH_THREADS), 0, stream, a);
+        hipLaunchKernelGGL(moe_dispatch_scan, dim3(1), dim3(SCAN_THREADS), 0, stream, a);
+        hipLaunchKernelGGL(moe_dispatch_scatter, dim3(a.num_chunks), dim3(DISPATCH_THREADS), 0, stream, a);
+    }
     hipLaunchKernelGGL(moe_dispatch_gather, dim3(gather_blocks), dim3(256), 0, stream, a);
 }
 
