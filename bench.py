@@ -110,6 +110,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--block-n", type=int, default=0)
     ap.add_argument("--l2-n-major", type=int, default=-1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -134,7 +135,7 @@ def main():
     T, H = inp["x"].shape
     y = torch.empty((T, H), dtype=torch.int16, device="cuda:0")
     layer = B.MegaMoE(work["E"], H, work["I"], work["k"], T, block_m=args.block_m,
-                      l2_n_major=args.l2_n_major)
+                      block_n=args.block_n, l2_n_major=args.l2_n_major)
     plan = B.mega_moe_plan(layer.cfg, T)
 
     def step():
@@ -195,7 +196,7 @@ def main():
     roof["traffic"] = RS.read_traffic(
         os.path.join(ROOT, "profiles", f"moe_expert_ffn_{name}_hbm_traffic.txt"), name)
     roof["algorithmic_bytes"] = work["expert_kernel_bytes"]
-    roof["kernel"] = f"moe_expert_ffn<{plan.block_m}>"
+    roof["kernel"] = f"moe_expert_ffn<{plan.block_m}x{plan.block_n}>"
     roof["kernel_ms"] = expert_ms
     out = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
@@ -203,7 +204,8 @@ def main():
         "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
         "config": {"workload": name, "tokens": T, "hidden": H, "intermediate": work["I"],
                    "experts": work["E"], "topk": work["k"], "routing": inp["workload"].routing,
-                   "block_m": plan.block_m, "l2_n_major": plan.l2_n_major},
+                   "block_m": plan.block_m, "block_n": plan.block_n,
+                   "l2_n_major": plan.l2_n_major},
         "tflops": tflops, "weight_stream_gbs": wgbs,
         "pct_roofline": 100.0 * t_roof / s,
         "kernel_ms": {"dispatch": float(k_ms[:, 0].mean()), "expert": expert_ms,

@@ -56,6 +56,12 @@ enum {
     L_COUNT
 };
 
+// 256-column tiles: both N extents must split into them, and the 32-row
+// instance has none (its rows do not divide over eight waves).
+bool wide_tiles_fit(const mega_moe_config& c) {
+    return (2 * c.intermediate) % 256 == 0 && c.hidden % 256 == 0 && c.block_m != 32;
+}
+
 int check_config(const mega_moe_config* c) {
     if (!c) return fail(MEGA_MOE_ERR_INVALID_ARG, "config is NULL");
     if (c->num_experts < 1 || c->num_experts > MAX_EXPERTS)
@@ -82,6 +88,11 @@ int check_config(const mega_moe_config* c) {
         return fail(MEGA_MOE_ERR_INVALID_ARG, "block_m must be 0, 32, 64 or 128");
     if (c->l2_n_major < -1 || c->l2_n_major > 1)
         return fail(MEGA_MOE_ERR_INVALID_ARG, "l2_n_major must be -1, 0 or 1");
+    if (c->block_n != 0 && c->block_n != 128 && c->block_n != 256)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "block_n must be 0, 128 or 256");
+    if (c->block_n == 256 && !wide_tiles_fit(*c))
+        return fail(MEGA_MOE_ERR_INVALID_ARG,
+                    "block_n 256 needs 2*intermediate and hidden multiples of 256 and block_m != 32");
     return MEGA_MOE_OK;
 }
 
@@ -135,11 +146,14 @@ void plan(const mega_moe_config& c, int32_t T, mega_moe_plan_info* p) {
     else bm = expected <= TIER_64_MAX ? 64 : 128;
     int nm = c.l2_n_major;
     if (nm < 0) nm = expected >= 256.0f ? 1 : 0;   // SM90 design 12.2
+    int bn = c.block_n ? c.block_n : 128;
+    if (bm == 32) bn = 128;
     p->expected_tokens_per_expert = expected;
     p->block_m = bm;
     p->l2_n_major = nm;
-    p->l1_n_blocks = 2 * c.intermediate / 128;
-    p->l2_n_blocks = c.hidden / 128;
+    p->block_n = bn;
+    p->l1_n_blocks = 2 * c.intermediate / bn;
+    p->l2_n_blocks = c.hidden / bn;
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -233,8 +247,6 @@ int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out) {
     a.E = cfg->num_experts;
     a.k = cfg->num_topk;
     a.P_cap = L.P_cap;
-    a.nb1 = 2 * cfg->intermediate / 128;
-    a.nb2 = cfg->hidden / 128;
     a.wait_spin_limit = 1u << 22;
     // gfx950 groups 32 compute units per XCD, each XCD with its own L2
     a.n_xcd = (h->num_cus % 32 == 0 && h->num_cus / 32 >= 1 && h->num_cus / 32 <= MAX_XCD)
@@ -295,6 +307,9 @@ int mega_moe_forward(mega_moe_handle* h, int32_t T, const uint8_t* x, const floa
     a.T = T;
     a.R = T * h->cfg.num_topk;
     a.block_m = p.block_m;
+    a.block_n = p.block_n;
+    a.nb1 = p.l1_n_blocks;
+    a.nb2 = p.l2_n_blocks;
     a.n_major = p.l2_n_major;
     a.xcd_group = p.block_m == 32 ? 4 : (p.block_m == 64 ? 2 : 4);
     a.num_chunks = (a.R + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK;

@@ -71,10 +71,8 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int BN = 128;              // output columns per tile
 constexpr int BK = 128;              // K bytes per step
-constexpr int NT = 256;              // threads per workgroup (4 waves)
-constexpr int MAX_W_SF = 64;         // weight scale blocks per tile (H/128, I/128 <= 64)
+constexpr int MAX_W_SF = 64;         // K scale blocks of a weight row block (H/128, I/128 <= 64)
 
 __device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c) {
     // scale operands 0 select the plain (unscaled) FP8 x FP8 instruction
@@ -213,35 +211,48 @@ __device__ __forceinline__ float dpp_move(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-template <int MS>
+// One instance per tile shape: BLOCK_M = 32 MS pool rows x BN output columns
+// (128 or 256).  A tile has BN/32 waves, one per 32-column group.
+template <int MS, int BNT>
 struct Cfg {
     static constexpr int BM = 32 * MS;                    // pool rows per tile
+    static constexpr int BN = BNT;                        // output columns per tile
+    static constexpr int NW = BN / 32;                    // waves per workgroup
+    static constexpr int NT = 64 * NW;                    // threads per workgroup
+    static constexpr int NSB = BN / 128;                  // 128-row weight scale blocks per tile
     static constexpr int A_BYTES = BM * BK;               // activation rows of a stage
     static constexpr int B_BYTES = BN * BK;               // weight rows of a stage
     static constexpr int SF_BYTES = 2 * BM * 4;           // per-row scales of a step (2 halves in L2)
     static constexpr int STAGE = A_BYTES + B_BYTES + SF_BYTES;
-    // Two workgroups share a CU (and each SIMD runs two waves), so each gets
-    // half of the 160 KB of LDS: 3 stages at 32- and 64-row tiles, 2 at
-    // 128-row tiles.  While one workgroup fills or drains its pipeline at a
-    // tile boundary, or waits for an L1 tile, the other keeps loading.
-    static constexpr int WPC = 2;
-    static constexpr int S = MS == 4 ? 2 : 3;
-    static constexpr int PT = (BM + BN) / 32;             // 1 KB row blocks per wave per step
+    // 128-column tiles: two workgroups share a CU (each SIMD runs one wave of
+    // each) with half of the 160 KB of LDS each: 3 stages at 32- and 64-row
+    // tiles, 2 at 128-row tiles.  256-column tiles: one eight-wave workgroup
+    // per CU (two waves per SIMD) with 3 stages.  While one workgroup (or
+    // wave) fills or drains its pipeline at a tile boundary, or waits for an
+    // L1 tile, the other keeps loading.
+    static constexpr int WPC = BN == 128 ? 2 : 1;
+    static constexpr int S = BN == 128 && MS == 4 ? 2 : 3;
+    static constexpr int PT = (BM + BN) / (8 * NW);       // 1 KB row blocks per wave per step
+    static constexpr int A_J = BM / (8 * NW);             // of which activation rows
     static constexpr int WAIT = (S - 2) * (PT + 1);       // loads younger than the current step
     static constexpr int OFF_TILE = S * STAGE;            // per-tile area after the stages
-    static constexpr int LDS_BYTES = OFF_TILE + MAX_W_SF * 4 + BM * 4 + 16;
+    static constexpr int HS = BN / 2 + 4;                 // L1 epilogue h row stride (floats)
+    static constexpr int LDS_BYTES = OFF_TILE + MAX_W_SF * NSB * 4 + BM * 4 + 16;
+    static_assert((BM + BN) % (8 * NW) == 0 && BM % (8 * NW) == 0, "row blocks per wave");
     static_assert(WAIT < 64, "vmcnt range");
     static_assert(WPC * LDS_BYTES <= 160 * 1024, "LDS per CU");
-    static_assert(BM * BN * 2 <= S * STAGE && BM * 68 * 4 <= S * STAGE, "epilogue buffers");
+    static_assert(BM * BN * 2 <= S * STAGE && BM * HS * 4 <= S * STAGE, "epilogue buffers");
 };
 
-template <int MS>
+template <int MS, int BNT>
 struct Lds {
+    using C = Cfg<MS, BNT>;
     uint8_t* base;
-    __device__ uint8_t* stage(int i) const { return base + i * Cfg<MS>::STAGE; }
-    __device__ float* w_sf() const { return reinterpret_cast<float*>(base + Cfg<MS>::OFF_TILE); }
-    __device__ float* row_w() const { return w_sf() + MAX_W_SF; }   // top-k weight per row (L1)
-    __device__ int* tile() const { return reinterpret_cast<int*>(row_w() + Cfg<MS>::BM); }
+    __device__ uint8_t* stage(int i) const { return base + i * C::STAGE; }
+    // weight scales of the tile: [NSB][KB]
+    __device__ float* w_sf() const { return reinterpret_cast<float*>(base + C::OFF_TILE); }
+    __device__ float* row_w() const { return w_sf() + MAX_W_SF * C::NSB; }   // top-k weight per row (L1)
+    __device__ int* tile() const { return reinterpret_cast<int*>(row_w() + C::BM); }
 };
 
 // Issues the direct loads of one step.  Wave w fills the 1 KB row blocks
@@ -252,12 +263,13 @@ struct Lds {
 // layout).  A step past the end (real = false) still issues the same number
 // of instructions, from lane 0 only, so every wave's count of outstanding
 // loads is the same at every step.
-template <int MS, int HALVES>
+template <int MS, int BNT, int HALVES>
 struct Loader {
+    using C = Cfg<MS, BNT>;
     // L2 tiles read the activations and scales their L1 tiles just wrote
     static constexpr int AUX_ACT = HALVES == 2 ? SC1 : 0;
-    static constexpr int PT = Cfg<MS>::PT;
-    static constexpr int Q = HALVES * Cfg<MS>::BM;        // scale bytes per wave (= 4 * rows / 4)
+    static constexpr int PT = C::PT;
+    static constexpr int Q = 4 * HALVES * C::BM / C::NW;  // scale bytes per wave
     __amdgpu_buffer_rsrc_t ra, rb, rs;
     int voff[PT];
     int sf_voff;
@@ -271,14 +283,14 @@ struct Loader {
         w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
         for (int j = 0; j < PT; ++j) {
-            const int n = 8 * (4 * j + w) + (lane >> 3);          // stage row
-            const int r = j < MS ? n : n - Cfg<MS>::BM;         // row of its operand
+            const int n = 8 * (C::NW * j + w) + (lane >> 3);     // stage row
+            const int r = j < C::A_J ? n : n - C::BM;           // row of its operand
             voff[j] = r * row_bytes + 16 * ((lane & 7) ^ row_swz(n));
         }
         // scale bytes [w*Q, w*Q + Q) of the step's 2*BM*4-byte scale area
         const int off = w * Q + 16 * lane;
-        const int half = off / (Cfg<MS>::BM * 4);
-        sf_voff = half * P * 4 + (off - half * Cfg<MS>::BM * 4);
+        const int half = off / (C::BM * 4);
+        sf_voff = half * P * 4 + (off - half * C::BM * 4);
         sf_step = HALVES * P * 4;
     }
 
@@ -288,12 +300,12 @@ struct Loader {
 #pragma unroll
         for (int j = 0; j < PT; ++j) {
             if (real || lane == 0) {
-                if (j < MS) dma16<AUX_ACT>(ra, stage + (4 * j + w) * 1024, voff[j], soff);
-                else dma16(rb, stage + (4 * j + w) * 1024, voff[j], soff);
+                if (j < C::A_J) dma16<AUX_ACT>(ra, stage + (C::NW * j + w) * 1024, voff[j], soff);
+                else dma16(rb, stage + (C::NW * j + w) * 1024, voff[j], soff);
             }
         }
         if (lane < Q / 16 && (real || lane == 0))
-            dma16<AUX_ACT>(rs, stage + Cfg<MS>::A_BYTES + Cfg<MS>::B_BYTES + w * Q, sf_voff,
+            dma16<AUX_ACT>(rs, stage + C::A_BYTES + C::B_BYTES + w * Q, sf_voff,
                   real ? kb * sf_step : 0);
     }
 };
@@ -305,15 +317,15 @@ __device__ __forceinline__ void wait_barrier() {
 }
 
 // K loop over KB steps; compute(stage, kb) reads only stage.
-template <int MS, int HALVES, typename Compute>
-__device__ __forceinline__ void k_loop(const Loader<MS, HALVES>& ld, const Lds<MS>& lds, int KB,
+template <int MS, int BNT, int HALVES, typename Compute>
+__device__ __forceinline__ void k_loop(const Loader<MS, BNT, HALVES>& ld, const Lds<MS, BNT>& lds, int KB,
                                        Compute&& compute) {
-    constexpr int S = Cfg<MS>::S;
+    constexpr int S = Cfg<MS, BNT>::S;
 #pragma unroll
     for (int d = 0; d < S - 1; ++d) ld.issue(lds.stage(d), d, d < KB);
     int cur = 0;
     for (int kb = 0; kb < KB; ++kb) {
-        wait_barrier<Cfg<MS>::WAIT>();
+        wait_barrier<Cfg<MS, BNT>::WAIT>();
         const int nk = kb + S - 1;
         ld.issue(lds.stage(cur == 0 ? S - 1 : cur - 1), nk, nk < KB);
         compute(lds.stage(cur), kb);
@@ -329,17 +341,20 @@ __device__ __forceinline__ void k_loop(const Loader<MS, HALVES>& ld, const Lds<M
 // column group's B operand are read and converted once for two output
 // blocks; any other tile gives wave w column group w over all active slices,
 // so no wave idles on a ragged tile.
-template <int MS, int ACT>
+template <int MS, int BNT, int ACT>
 struct Lay {
     static constexpr bool GRID = MS == 4 && ACT == 4;
     static constexpr int NJ = GRID ? 2 : ACT;     // 32-row slices per wave
     static constexpr int NG = GRID ? 2 : 1;       // 32-column groups per wave
+    static constexpr int WC = Cfg<MS, BNT>::NW / 2;   // column-group pairs (GRID)
     int s0, g0;
     __device__ Lay() {
         const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        s0 = GRID ? 2 * (w >> 1) : 0;
-        g0 = GRID ? 2 * (w & 1) : w;
+        s0 = GRID ? 2 * (w / WC) : 0;
+        g0 = GRID ? 2 * (w % WC) : w;
     }
+    // the 128-row weight scale block of this wave's column groups
+    __device__ int sblock() const { return g0 >> 2; }
 };
 
 template <int N>
@@ -363,21 +378,23 @@ __device__ __forceinline__ void dispatch_act(int act, Fn&& fn) {
 // ---------------------------------------------------------------------------
 // L1 tile: pool rows [row0, row0 + valid) of expert e, W1 N block nb.
 // ---------------------------------------------------------------------------
-template <int MS>
-__device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int row0, int valid,
-                        int nb) {
-    constexpr int BM = Cfg<MS>::BM;
+template <int MS, int BNT>
+__device__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT>& lds, int e, int pb, int row0,
+                        int valid, int nb) {
+    using C = Cfg<MS, BNT>;
+    constexpr int BM = C::BM, BN = C::BN, NT = C::NT;
     const int H = a.H;
     const int KB = H / BK;
     const size_t P = a.P_cap;
     const int c = threadIdx.x & 31;
     const int act = min(MS, (valid + 31) / 32);
 
-    const float* wsf = a.w1_sf + ((size_t)e * a.nb1 + nb) * KB;
-    for (int i = threadIdx.x; i < KB; i += NT) lds.w_sf()[i] = wsf[i];
+    // the tile's NSB weight scale rows of W1_sf [E, 2I/128, H/128], contiguous
+    const float* wsf = a.w1_sf + ((size_t)e * a.nb1 + nb) * C::NSB * KB;
+    for (int i = threadIdx.x; i < C::NSB * KB; i += NT) lds.w_sf()[i] = wsf[i];
     for (int r = threadIdx.x; r < BM; r += NT) lds.row_w()[r] = a.l1_w[row0 + r];
     __syncthreads();
-    const Loader<MS, 1> ld(make_rsrc(a.l1_acts + (size_t)row0 * H, (uint32_t)valid * H),
+    const Loader<MS, BNT, 1> ld(make_rsrc(a.l1_acts + (size_t)row0 * H, (uint32_t)valid * H),
                            make_rsrc(a.w1 + ((size_t)e * (2 * a.I) + (size_t)nb * BN) * H,
                                      (uint32_t)BN * H),
                            H, make_rsrc(a.l1_sf + row0, (uint32_t)(((KB - 1) * P + BM) * 4)),
@@ -386,19 +403,19 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
     const v16f zero = v16f{};
     // ---- epilogue buffer: h of the tile, written from the accumulators ----
     // Lane c < 8 (mod 16) of a column group holds a gate value and lane c + 8
-    // the up value of the same output, 16g + 8*(c/16) + c%8 of the tile's 64
-    // for column group g; one DPP rotation within each row of 16 lanes brings
+    // the up value of the same output, 16g + 8*(c/16) + c%8 of the tile's
+    // BN/2 for column group g; one DPP rotation within each row of 16 lanes brings
     // them together.  silu(g) = g / (1 + 2^(-g*log2 e)) with the hardware exp2
     // and reciprocal (a few float32 ulps; the code rule tolerates them).  h
     // goes to LDS; then one thread per 16 outputs of a row takes the row amax
     // over its quad of threads (DPP), the exactly rounded scale amax / 448,
     // and writes 16 codes (h * (1 / sf)) as one store.
-    constexpr int HS = 68;                                              // h row stride (floats)
+    constexpr int HS = C::HS;                                           // h row stride (floats)
     float* hbuf = reinterpret_cast<float*>(lds.stage(0));              // [BM][HS]
 
     dispatch_act<MS>(act, [&](auto tag) {
         constexpr int ACT = decltype(tag)::value;
-        using LY = Lay<MS, ACT>;
+        using LY = Lay<MS, BNT, ACT>;
         const LY ly;
         v16f acc[LY::NJ][LY::NG];
 #pragma unroll
@@ -406,9 +423,9 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
 #pragma unroll
             for (int q = 0; q < LY::NG; ++q) acc[j][q] = v16f{};
 
-        k_loop<MS, 1>(ld, lds, KB, [&](const uint8_t* stg, int kb) {
-            const float sw = lds.w_sf()[kb];
-            const uint8_t* sfa = stg + Cfg<MS>::A_BYTES + Cfg<MS>::B_BYTES;
+        k_loop<MS, BNT, 1>(ld, lds, KB, [&](const uint8_t* stg, int kb) {
+            const float sw = lds.w_sf()[ly.sblock() * KB + kb];
+            const uint8_t* sfa = stg + C::A_BYTES + C::B_BYTES;
             if constexpr (LY::GRID) {
                 // eight 16-K parts; per part the B operands of the two column
                 // groups and the A operand of each slice are read and
@@ -419,7 +436,7 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
                     v8h b16[LY::NG];
 #pragma unroll
                     for (int q = 0; q < LY::NG; ++q)
-                        b16[q] = f16_frag_part(stg + Cfg<MS>::A_BYTES, ly.g0 + q, p);
+                        b16[q] = f16_frag_part(stg + C::A_BYTES, ly.g0 + q, p);
 #pragma unroll
                     for (int j = 0; j < LY::NJ; ++j) {
                         const v8h a16 = f16_frag_part(stg, ly.s0 + j, p);
@@ -438,7 +455,7 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
             } else {
                 // one column group: its B operand converted once per step,
                 // then one MFMA chain per active slice
-                const Frag fb = read_frag2(stg + Cfg<MS>::A_BYTES, ly.g0);
+                const Frag fb = read_frag2(stg + C::A_BYTES, ly.g0);
                 v8h b16[8];
 #pragma unroll
                 for (int p = 0; p < 8; ++p) b16[p] = f16_part(fb.h[p >> 2], p & 3);
@@ -476,8 +493,11 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
     });
 
     __syncthreads();
-    for (int t = threadIdx.x; t < 4 * BM; t += NT) {            // NT is a multiple of 4: quads stay whole
-        const int r = t >> 2, part = t & 3;
+    // BN/32 threads per row, 16 outputs each; the 4 of one 64-output scale
+    // group are consecutive lanes (NT and BN/32 are multiples of 4)
+    constexpr int PPR = BN / 32;
+    for (int t = threadIdx.x; t < PPR * BM; t += NT) {
+        const int r = t / PPR, part = t % PPR;
         const float4* src4 = reinterpret_cast<const float4*>(hbuf + r * HS + 16 * part);
         float hv[16];
 #pragma unroll
@@ -503,9 +523,9 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
             code[q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, d, true);
         }
         if (r < valid) {
-            *reinterpret_cast<uint4*>(a.l2_acts + (size_t)(row0 + r) * a.I + nb * 64 + part * 16) =
-                uint4{code[0], code[1], code[2], code[3]};
-            if (part == 0) a.l2_sf[(size_t)nb * P + row0 + r] = sf;
+            *reinterpret_cast<uint4*>(a.l2_acts + (size_t)(row0 + r) * a.I + nb * (BN / 2) +
+                                      part * 16) = uint4{code[0], code[1], code[2], code[3]};
+            if ((part & 3) == 0) a.l2_sf[(size_t)(nb * C::NSB + (part >> 2)) * P + row0 + r] = sf;
         }
     }
     // publish: the vector L1 writes through, so once every thread's stores are
@@ -519,18 +539,20 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
 // ---------------------------------------------------------------------------
 // L2 tile: pool rows [row0, row0 + valid) of expert e, W2 N block nb.
 // ---------------------------------------------------------------------------
-template <int MS>
-__device__ void l2_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int row0, int valid,
-                        int nb) {
-    constexpr int BM = Cfg<MS>::BM;
+template <int MS, int BNT>
+__device__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT>& lds, int e, int pb, int row0,
+                        int valid, int nb) {
+    using C = Cfg<MS, BNT>;
+    constexpr int BM = C::BM, BN = C::BN, NT = C::NT;
     const int I = a.I;
     const int KB = I / BK;
     const size_t P = a.P_cap;
     const int c = threadIdx.x & 31;
     const int act = min(MS, (valid + 31) / 32);
 
-    const float* wsf = a.w2_sf + ((size_t)e * a.nb2 + nb) * KB;
-    for (int i = threadIdx.x; i < KB; i += NT) lds.w_sf()[i] = wsf[i];
+    // the tile's NSB weight scale rows of W2_sf [E, H/128, I/128], contiguous
+    const float* wsf = a.w2_sf + ((size_t)e * a.nb2 + nb) * C::NSB * KB;
+    for (int i = threadIdx.x; i < C::NSB * KB; i += NT) lds.w_sf()[i] = wsf[i];
     // wait until every L1 tile of this pool block has published
     if (threadIdx.x == 0) {
         uint32_t spins = 0;
@@ -545,7 +567,7 @@ __device__ void l2_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
     }
     __syncthreads();
 
-    const Loader<MS, 2> ld(make_rsrc(a.l2_acts + (size_t)row0 * I, (uint32_t)valid * I),
+    const Loader<MS, BNT, 2> ld(make_rsrc(a.l2_acts + (size_t)row0 * I, (uint32_t)valid * I),
                            make_rsrc(a.w2 + ((size_t)e * a.H + (size_t)nb * BN) * I, (uint32_t)BN * I),
                            I, make_rsrc(a.l2_sf + row0, (uint32_t)(((2 * KB - 1) * P + BM) * 4)),
                            (int)P);
@@ -555,7 +577,7 @@ __device__ void l2_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
 
     dispatch_act<MS>(act, [&](auto tag) {
         constexpr int ACT = decltype(tag)::value;
-        using LY = Lay<MS, ACT>;
+        using LY = Lay<MS, BNT, ACT>;
         const LY ly;
         v16f acc[LY::NJ][LY::NG];
 #pragma unroll
@@ -563,12 +585,12 @@ __device__ void l2_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
 #pragma unroll
             for (int q = 0; q < LY::NG; ++q) acc[j][q] = v16f{};
 
-        k_loop<MS, 2>(ld, lds, KB, [&](const uint8_t* stg, int kb) {
-            const float sw = lds.w_sf()[kb];
-            const uint8_t* sfa = stg + Cfg<MS>::A_BYTES + Cfg<MS>::B_BYTES;
+        k_loop<MS, BNT, 2>(ld, lds, KB, [&](const uint8_t* stg, int kb) {
+            const float sw = lds.w_sf()[ly.sblock() * KB + kb];
+            const uint8_t* sfa = stg + C::A_BYTES + C::B_BYTES;
             Frag fb[LY::NG];
 #pragma unroll
-            for (int q = 0; q < LY::NG; ++q) fb[q] = read_frag2(stg + Cfg<MS>::A_BYTES, ly.g0 + q);
+            for (int q = 0; q < LY::NG; ++q) fb[q] = read_frag2(stg + C::A_BYTES, ly.g0 + q);
 #pragma unroll
             for (int j = 0; j < LY::NJ; ++j) {
                 const int sl = ly.s0 + j;
@@ -596,8 +618,8 @@ __device__ void l2_tile(const MoeArgs& a, const Lds<MS>& lds, int e, int pb, int
                         bf16_rne(acc[j][q][v]);
     });
     __syncthreads();
-    for (int q = threadIdx.x; q < BM * 16; q += NT) {
-        const int r = q >> 4, part = q & 15;
+    for (int q = threadIdx.x; q < BM * (BN / 8); q += NT) {
+        const int r = q / (BN / 8), part = q % (BN / 8);
         if (r < valid) {
             const int f = a.src[row0 + r];
             if (f >= 0) {
@@ -628,12 +650,12 @@ __device__ __forceinline__ void tile_coords(int u, int cnt, int nbs, int G, bool
 // Two workgroups of four waves per CU, one wave of each per SIMD; the launch
 // puts num_cus * 2 of them in flight and they take tiles until their XCD's
 // queue is empty.
-template <int MS>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Cfg<MS>::WPC)))
+template <int MS, int BNT>
+__global__ void __launch_bounds__((Cfg<MS, BNT>::NT)) __attribute__((amdgpu_waves_per_eu(2)))
 moe_expert_ffn(MoeArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg<MS>::LDS_BYTES];
-    const Lds<MS> lds{smem};
-    constexpr int BM = Cfg<MS>::BM;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg<MS, BNT>::LDS_BYTES];
+    const Lds<MS, BNT> lds{smem};
+    constexpr int BM = Cfg<MS, BNT>::BM;
     // XCC_ID hardware register, bits [3:0]
     const int xcd = (__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xf) % a.n_xcd;
     const int G = a.xcd_group;
@@ -655,31 +677,36 @@ moe_expert_ffn(MoeArgs a) {
         const int m_local = pb - __builtin_amdgcn_readfirstlane(a.mb_start[e]);
         const int row0 = __builtin_amdgcn_readfirstlane(a.offsets[e]) + m_local * BM;
         const int valid = min(BM, __builtin_amdgcn_readfirstlane(a.counts[e]) - m_local * BM);
-        if (is_l1) l1_tile<MS>(a, lds, e, pb, row0, valid, nb);
-        else l2_tile<MS>(a, lds, e, pb, row0, valid, nb);
+        if (is_l1) l1_tile<MS, BNT>(a, lds, e, pb, row0, valid, nb);
+        else l2_tile<MS, BNT>(a, lds, e, pb, row0, valid, nb);
         __syncthreads();
     }
 }
 
-template <int MS>
+template <int MS, int BNT>
 static int launch_one(const MoeArgs& a, int num_cus, hipStream_t stream) {
+    constexpr int NT = Cfg<MS, BNT>::NT;
     static int per_cu = 0;   // occupancy of this instance (same on every call)
     if (per_cu == 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_expert_ffn<MS>, NT, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_expert_ffn<MS, BNT>, NT, 0) !=
                 hipSuccess || n < 1)
             n = 1;
         per_cu = n;
     }
-    hipLaunchKernelGGL(moe_expert_ffn<MS>, dim3(num_cus * per_cu), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((moe_expert_ffn<MS, BNT>), dim3(num_cus * per_cu), dim3(NT), 0, stream, a);
     return num_cus * per_cu;
 }
 
 int launch_expert_ffn(const MoeArgs& a, int num_cus, hipStream_t stream) {
+    if (a.block_n == 256) {
+        if (a.block_m == 64) return launch_one<2, 256>(a, num_cus, stream);
+        return launch_one<4, 256>(a, num_cus, stream);
+    }
     switch (a.block_m) {
-        case 32: return launch_one<1>(a, num_cus, stream);
-        case 64: return launch_one<2>(a, num_cus, stream);
-        default: return launch_one<4>(a, num_cus, stream);
+        case 32: return launch_one<1, 128>(a, num_cus, stream);
+        case 64: return launch_one<2, 128>(a, num_cus, stream);
+        default: return launch_one<4, 128>(a, num_cus, stream);
     }
 }
 

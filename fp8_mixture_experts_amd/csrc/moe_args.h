@@ -23,8 +23,9 @@ struct MoeArgs {
     int32_t R;          // T * k routes
     int64_t P_cap;      // pool rows allocated (row stride of the pool-minor arrays)
     int32_t block_m;    // rows per pool block for the expert kernel
-    int32_t nb1;        // L1 N blocks: 2I / 128
-    int32_t nb2;        // L2 N blocks: H / 128
+    int32_t block_n;    // output columns per expert-kernel tile (128 or 256)
+    int32_t nb1;        // L1 N blocks: 2I / block_n
+    int32_t nb2;        // L2 N blocks: H / block_n
     int32_t n_major;    // L2 tile order: 1 = consecutive tiles share a W2 N block
     int32_t num_chunks; // dispatch chunks of DISPATCH_CHUNK routes
     uint32_t wait_spin_limit;  // bound on one L2 tile's wait for its L1 tiles

@@ -69,6 +69,9 @@ typedef struct mega_moe_config {
     int32_t fast_math;        /* 0: accurate exp and division in SwiGLU (only 0) */
     int32_t block_m;          /* 0 = automatic (SM90 design 13.1), else 32/64/128 */
     int32_t l2_n_major;       /* -1 automatic (12.2), 0 M-major, 1 N-major L2 order */
+    int32_t block_n;          /* output columns per expert-kernel tile: 0 = automatic,
+                                 128, or 256 (needs 2I % 256 == 0, H % 256 == 0 and
+                                 block_m != 32) */
 } mega_moe_config;
 
 typedef struct mega_moe_handle mega_moe_handle;
@@ -132,16 +135,18 @@ int32_t mega_moe_token_alignment(void);
 
 /*
  * Host plan of one call (SM90 design 12.2 and 13.1): expected routes per
- * expert T*k/E, BLOCK_M (<= 16.5 -> 32, <= 64.5 -> 64, else 128, unless
- * cfg->block_m forces one) and whether the L2 tiles run N-major (expected >=
- * 256, unless forced).  Host-only; needs no GPU.
+ * expert T*k/E; BLOCK_M chosen from it (thresholds measured for this kernel
+ * on MI355X: <= 50.5 -> 64, else 128) unless cfg->block_m forces one; the
+ * tile width block_n (unless cfg->block_n forces one); and whether the tiles
+ * run N-major (expected >= 256, unless forced).  Host-only; needs no GPU.
  */
 typedef struct mega_moe_plan_info {
     float expected_tokens_per_expert;
     int32_t block_m;
     int32_t l2_n_major;
-    int32_t l1_n_blocks;      /* 2I / 128 */
-    int32_t l2_n_blocks;      /* H / 128  */
+    int32_t l1_n_blocks;      /* 2I / block_n: L1 tiles per pool block */
+    int32_t l2_n_blocks;      /* H / block_n: L2 tiles per pool block */
+    int32_t block_n;          /* output columns per expert-kernel tile */
 } mega_moe_plan_info;
 int mega_moe_plan(const mega_moe_config* cfg, int32_t num_tokens, mega_moe_plan_info* out);
 

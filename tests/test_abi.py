@@ -55,7 +55,7 @@ def test_plan_matches_golden_tiers():
         p = B.mega_moe_plan(cfg, int(t))
         assert math.isclose(p.expected_tokens_per_expert, float(exp), rel_tol=1e-6)
         assert (p.block_m, p.l2_n_major) == (int(bm), int(nm)), (t, k, e)
-        assert p.l1_n_blocks == 2 * 2048 // 128 and p.l2_n_blocks == 7168 // 128
+        assert p.l1_n_blocks == 2 * 2048 // p.block_n and p.l2_n_blocks == 7168 // p.block_n
 
 
 def test_plan_overrides():
@@ -63,11 +63,17 @@ def test_plan_overrides():
     assert p.block_m == 32 and p.l2_n_major == 1
     p = B.mega_moe_plan(_cfg(block_m=128, l2_n_major=0), 1)
     assert p.block_m == 128 and p.l2_n_major == 0
+    p = B.mega_moe_plan(_cfg(block_m=64, block_n=256), 128)
+    assert p.block_n == 256 and p.l1_n_blocks == 16 and p.l2_n_blocks == 28
+    p = B.mega_moe_plan(_cfg(block_m=128, block_n=128), 8192)
+    assert p.block_n == 128 and p.l1_n_blocks == 32 and p.l2_n_blocks == 56
 
 
 @pytest.mark.parametrize("kw", [dict(hidden=100), dict(intermediate=192), dict(num_topk=0),
                                 dict(num_experts=0), dict(num_experts=5000), dict(max_tokens=-1),
-                                dict(block_m=48), dict(l2_n_major=2)])
+                                dict(block_m=48), dict(l2_n_major=2), dict(block_n=192),
+                                dict(block_m=32, block_n=256),
+                                dict(hidden=7296, block_n=256)])
 def test_invalid_configs_are_rejected(kw):
     assert B.mega_moe_workspace_bytes(_cfg(**kw)) == -1
     with pytest.raises(B.MegaMoEError) as ei:

@@ -68,16 +68,38 @@ def test_layer_matches_oracle(name):
         run.close()
 
 
+@pytest.mark.parametrize("name", ["many_blocks", "skewed", "tiny"])
+def test_wide_tiles_match_oracle(name):
+    inp, ref = _case(name)
+    for bm in (64, 128):
+        run = G.Runner(inp, block_m=bm, block_n=256)
+        try:
+            assert run.forward() == 0
+            _compare_all(inp, ref, run, f"{name} block_m {bm} block_n 256")
+        finally:
+            run.close()
+
+
+def _tile_shapes(inp):
+    """(block_m, block_n) pairs the library accepts for this shape."""
+    H = inp["x"].shape[1]
+    I = inp["w2"].shape[2]
+    wide = H % 256 == 0 and (2 * I) % 256 == 0
+    return [(bm, bn) for bm in (32, 64, 128) for bn in (128, 256)
+            if bn == 128 or (wide and bm != 32)]
+
+
 @pytest.mark.parametrize("name", ["ragged", "many_blocks", "skewed"])
-def test_block_m_and_l2_order_do_not_change_results(name):
+def test_tile_shape_and_l2_order_do_not_change_results(name):
     inp, ref = _case(name)
     outs = []
-    for bm in (32, 64, 128):
+    for bm, bn in _tile_shapes(inp):
         for nm in (0, 1):
-            run = G.Runner(inp, block_m=bm, l2_n_major=nm)
+            run = G.Runner(inp, block_m=bm, block_n=bn, l2_n_major=nm)
             try:
                 assert run.forward() == 0
-                outs.append(((bm, nm), run.y().copy(), run.views(inp["x"].shape[0])["l2_acts"]))
+                outs.append(((bm, bn, nm), run.y().copy(),
+                             run.views(inp["x"].shape[0])["l2_acts"]))
             finally:
                 run.close()
     for key, y, l2 in outs[1:]:
