@@ -23,9 +23,14 @@ reason, in the design notes of the repository):
   sums the BF16 partials of the active slots in float32, in slot order, and
   casts the sum to BF16 (§11.2; "PR357 review" §6.3).
 * A slot is active when 0 <= topk_idx < E; others are skipped everywhere.
+* The optional activation clamp (a finite float32 ``clamp``) clamps the gate
+  and the up value to [-clamp, clamp] before SiLU (§10.1 step 3); +inf is no
+  clamp, the default.
 * Pool segments of each expert start at multiples of 128 and routes keep
   ascending flat order inside their expert's segment.
 """
+
+import math
 
 import numpy as np
 
@@ -121,12 +126,14 @@ def l1_gemm(a_codes, a_sf, w1_codes, w1_sf):
     return acc
 
 
-def swiglu_weighted(acc, topk_w):
+def swiglu_weighted(acc, topk_w, clamp=math.inf):
     """h[r, i] = silu(gate) * up * topk_w[r] on the interleaved L1 output.
 
     Output i takes its gate from stored column 16*(i//8) + i%8 and its up from
     16*(i//8) + 8 + i%8 ("SM90 design" §15.1); silu(g) = g / (1 + exp(-g))
-    (§10.1 step 3; no clamp).
+    (§10.1 step 3).  With a finite ``clamp`` the gate and the up value are
+    each first clamped to [-clamp, clamp] (§10.1 step 3, the activation clamp
+    option); +inf means no clamp.
     """
     m, N = acc.shape
     I = N // 2
@@ -135,6 +142,10 @@ def swiglu_weighted(acc, topk_w):
     up_col = gate_col + GATE_UP_GRANULE
     g = acc[:, gate_col]
     u = acc[:, up_col]
+    if math.isfinite(clamp):
+        c = float(clamp)
+        g = np.clip(g, -c, c)
+        u = np.clip(u, -c, c)
     with np.errstate(over="ignore"):
         silu = g / (1.0 + np.exp(-g))
     return silu * u * np.asarray(topk_w, np.float64)[:, None]
@@ -185,7 +196,7 @@ def l2_gemm(a_codes, a_sf64, w2_codes, w2_sf):
     return acc
 
 
-def expert_rows(a_codes, a_sf, topk_w, w1_codes, w1_sf, w2_codes, w2_sf):
+def expert_rows(a_codes, a_sf, topk_w, w1_codes, w1_sf, w2_codes, w2_sf, clamp=math.inf):
     """The whole per-route expert computation for some rows of one expert.
 
     Rows are independent, so this serves the full layer (all rows of an
@@ -194,7 +205,7 @@ def expert_rows(a_codes, a_sf, topk_w, w1_codes, w1_sf, w2_codes, w2_sf):
     ``part`` [m, H] uint16 BF16.
     """
     acc1 = l1_gemm(a_codes, a_sf, w1_codes, w1_sf)
-    h = swiglu_weighted(acc1, topk_w)
+    h = swiglu_weighted(acc1, topk_w, clamp)
     codes, sf = quantize_per64(h)
     acc2 = l2_gemm(codes, sf.astype(np.float64), w2_codes, w2_sf)
     part = bf16_rne(f32(acc2))
@@ -225,7 +236,7 @@ def combine(part_by_route, active):
 # The whole layer
 # --------------------------------------------------------------------------
 
-def forward(inp):
+def forward(inp, clamp=math.inf):
     """Full layer on one GPU's share: all routes local.
 
     ``inp`` holds x [T,H] uint8, x_sf [T,H/128] f32, topk_idx [T,k] int32,
@@ -252,7 +263,7 @@ def forward(inp):
             continue
         rows = np.arange(disp["offsets"][e], disp["offsets"][e] + c)
         out = expert_rows(pool["l1_acts"][rows], pool["l1_acts_sf"][:, rows].T,
-                          pool["l1_w"][rows], w1[e], w1_sf[e], w2[e], w2_sf[e])
+                          pool["l1_w"][rows], w1[e], w1_sf[e], w2[e], w2_sf[e], clamp)
         l2_acts[rows] = out["l2_acts"]
         l2_acts_sf[:, rows] = out["l2_acts_sf"].T
         comb[disp["src"][rows]] = out["part"]
@@ -263,7 +274,7 @@ def forward(inp):
     return res
 
 
-def forward_tokens(inp, tokens):
+def forward_tokens(inp, tokens, clamp=math.inf):
     """``y`` rows of the given tokens only, plus their per-route results.
 
     Each token's output depends only on its own routes, so a sample of tokens
@@ -286,7 +297,7 @@ def forward_tokens(inp, tokens):
         ts = np.array([t for t, _ in lst])
         js = np.array([j for _, j in lst])
         out = expert_rows(x[ts], x_sf[ts], topk_w[ts, js], inp["w1"][e],
-                          inp["w1_sf"][e], inp["w2"][e], inp["w2_sf"][e])
+                          inp["w1_sf"][e], inp["w2"][e], inp["w2_sf"][e], clamp)
         for n, (t, j) in enumerate(lst):
             per_route[(t, j)] = {key: val[n] for key, val in out.items()}
     result = {}

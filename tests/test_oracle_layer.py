@@ -17,6 +17,7 @@ combine (§11.2).  Each is tied here to something other than the oracle:
 """
 
 import decimal
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -43,7 +44,7 @@ def _dec(fr: Fraction) -> decimal.Decimal:
     return decimal.Decimal(fr.numerator) / decimal.Decimal(fr.denominator)
 
 
-def brute_layer(inp):
+def brute_layer(inp, clamp=None):
     x, x_sf = inp["x"], inp["x_sf"]
     idx, tw = inp["topk_idx"], inp["topk_weights"]
     w1, w1_sf, w2, w2_sf = inp["w1"], inp["w1_sf"], inp["w2"], inp["w2_sf"]
@@ -71,6 +72,10 @@ def brute_layer(inp):
             for i in range(I):
                 g = acc[16 * (i // 8) + i % 8]
                 u = acc[16 * (i // 8) + 8 + i % 8]
+                if clamp is not None:
+                    c = Fraction(clamp)
+                    g = max(-c, min(c, g))
+                    u = max(-c, min(c, u))
                 gd = _dec(g)
                 silu = gd / (1 + (-gd).exp())
                 h.append(Fraction(silu * _dec(u) * _dec(Fraction(float(tw[t, j])))))
@@ -128,6 +133,54 @@ def test_layer_matches_exact_brute_force():
     yf = codecs.bf16_to_f32(out["y"])
     for t in range(4):
         assert [Fraction(float(v)) for v in yf[t]] == y[t]
+
+
+@pytest.mark.slow
+def test_layer_with_activation_clamp_matches_exact_brute_force():
+    """The clamp (0.25, below most |gate| and |up| of these inputs) in the
+    float64 oracle against the exact layer with the clamp applied in rationals."""
+    wl = S.custom(tokens=3, hidden=128, intermediate=128, experts=2, topk=2, seed=21,
+                  weight_seed=22, weight_std=0.05)
+    inp = S.make_inputs(wl)
+    clamp = 0.25
+    acc = moe.l1_gemm(inp["x"][:1], inp["x_sf"][:1], inp["w1"][int(inp["topk_idx"][0, 0])],
+                      inp["w1_sf"][int(inp["topk_idx"][0, 0])])
+    assert np.mean(np.abs(acc) > clamp) > 0.3          # the clamp really bites
+    out = moe.forward(inp, clamp=clamp)
+    routes, y = brute_layer(inp, clamp=clamp)
+    for (t, j), r in routes.items():
+        s = out["slot_map"][t, j]
+        assert list(out["l2_acts"][s]) == r["codes"]
+        assert [Fraction(float(v)) for v in out["l2_acts_sf"][:, s]] == r["sf"]
+    yf = codecs.bf16_to_f32(out["y"])
+    for t in range(3):
+        assert [Fraction(float(v)) for v in yf[t]] == y[t]
+
+
+def test_clamp_at_or_above_every_value_changes_nothing():
+    rng = np.random.default_rng(31)
+    acc = rng.normal(0, 3, (5, 256))
+    w = rng.uniform(0.1, 1, 5)
+    ref = moe.swiglu_weighted(acc, w)
+    assert np.array_equal(moe.swiglu_weighted(acc, w, clamp=float(np.abs(acc).max())), ref)
+    assert np.array_equal(moe.swiglu_weighted(acc, w, clamp=1e30), ref)
+
+
+def test_saturated_clamp_gives_four_values():
+    """Every gate and up beyond +-c: h / w takes only +-c*s(c) and +-c*s(-c),
+    with the logistic s computed here through tanh."""
+    rng = np.random.default_rng(32)
+    c = 1.5
+    acc = rng.choice([-1, 1], (4, 256)) * rng.uniform(2.0, 9.0, (4, 256))
+    w = rng.uniform(0.1, 1, 4)
+    h = moe.swiglu_weighted(acc, w, clamp=c) / w[:, None]
+    sig = lambda v: 0.5 * (1.0 + math.tanh(v / 2.0))
+    pos, neg = c * sig(c), -c * sig(-c)       # silu(c), silu(-c)
+    want = {round(v, 12) for v in (pos * c, -pos * c, neg * c, -neg * c)}
+    assert {round(v, 12) for v in h.ravel()} <= want
+    # gate > c and up > c gives silu(c) * c
+    sel = (acc[:, 0:8] > 0) & (acc[:, 8:16] > 0)
+    assert np.allclose(h[:, 0:8][sel], pos * c, rtol=0, atol=1e-12)
 
 
 # --------------------------------------------------------------------------
