@@ -81,9 +81,10 @@ int check_config(const mega_moe_config* c) {
     if (c->max_tokens < 0) return fail(MEGA_MOE_ERR_INVALID_ARG, "max_tokens must be >= 0");
     if ((int64_t)c->max_tokens * c->num_topk > (int64_t)1 << 30)
         return fail(MEGA_MOE_ERR_INVALID_ARG, "max_tokens * num_topk too large");
-    if (!(std::isinf(c->activation_clamp) && c->activation_clamp > 0))
-        return fail(MEGA_MOE_ERR_UNSUPPORTED, "only activation_clamp = +inf (no clamp) is built");
-    if (c->fast_math != 0) return fail(MEGA_MOE_ERR_UNSUPPORTED, "only fast_math = 0 is built");
+    if (!(c->activation_clamp > 0))        // also rejects NaN
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "activation_clamp must be > 0 (+inf: no clamp)");
+    if (c->fast_math != 0 && c->fast_math != 1)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "fast_math must be 0 or 1");
     if (c->block_m != 0 && c->block_m != 32 && c->block_m != 64 && c->block_m != 128)
         return fail(MEGA_MOE_ERR_INVALID_ARG, "block_m must be 0, 32, 64 or 128");
     if (c->l2_n_major < -1 || c->l2_n_major > 1)
@@ -248,6 +249,8 @@ int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out) {
     a.k = cfg->num_topk;
     a.P_cap = L.P_cap;
     a.wait_spin_limit = 1u << 22;
+    a.act_clamp = cfg->activation_clamp;
+    a.fast_math = cfg->fast_math;
     // gfx950 groups 32 compute units per XCD, each XCD with its own L2
     a.n_xcd = (h->num_cus % 32 == 0 && h->num_cus / 32 >= 1 && h->num_cus / 32 <= MAX_XCD)
                   ? h->num_cus / 32 : 1;

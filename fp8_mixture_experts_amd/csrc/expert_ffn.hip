@@ -205,6 +205,23 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// silu(g) * u of one output: the optional activation clamp of both values
+// ("MegaMoE SM90 Implementation Design (Final)" 10.1 step 3; +inf leaves
+// every finite value unchanged), then g / (1 + e^-g), with the accurate expf
+// and an IEEE division, or with the hardware exp2 and reciprocal (a few
+// float32 ulps) when FAST.
+template <bool FAST>
+__device__ __forceinline__ float silu_up(float g, float u, float clamp) {
+    g = fminf(fmaxf(g, -clamp), clamp);
+    u = fminf(fmaxf(u, -clamp), clamp);
+    if constexpr (FAST) {
+        const float ex = __builtin_amdgcn_exp2f(-g * 1.44269504088896340736f);
+        return g * __builtin_amdgcn_rcpf(1.0f + ex) * u;
+    } else {
+        return g / (1.0f + expf(-g)) * u;
+    }
+}
+
 // The value of another lane by a DPP move (CTRL: quad_perm or row_ror).
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float x) {
@@ -379,7 +396,7 @@ __device__ __forceinline__ void dispatch_act(int act, Fn&& fn) {
 // L1 tile: pool rows [row0, row0 + valid) of expert e, W1 N block nb.
 // ---------------------------------------------------------------------------
 template <int MS, int BNT>
-__device__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT>& lds, int e, int pb, int row0,
+__device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT>& lds, int e, int pb, int row0,
                         int valid, int nb) {
     using C = Cfg<MS, BNT>;
     constexpr int BM = C::BM, BN = C::BN, NT = C::NT;
@@ -473,23 +490,27 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT>& lds, int e, int pb
 
         // the k loop ended with a barrier, so the stages are free for h
         const bool gate_lane = (c & 8) == 0;
+        auto write_h = [&](auto fast) {
+            constexpr bool FAST = decltype(fast)::value != 0;
 #pragma unroll
-        for (int j = 0; j < LY::NJ; ++j) {
-            const int sl = ly.s0 + j;
-            const v16f wt = row_vec(lds.row_w() + 32 * sl);
+            for (int j = 0; j < LY::NJ; ++j) {
+                const int sl = ly.s0 + j;
+                const v16f wt = row_vec(lds.row_w() + 32 * sl);
 #pragma unroll
-            for (int q = 0; q < LY::NG; ++q) {
-                const int col = 16 * (ly.g0 + q) + 8 * ((c >> 4) & 1) + (c & 7);
+                for (int q = 0; q < LY::NG; ++q) {
+                    const int col = 16 * (ly.g0 + q) + 8 * ((c >> 4) & 1) + (c & 7);
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const float x = acc[j][q][v];
-                    const float y = dpp_move<0x128>(x);                 // row_ror:8 = lane c ^ 8
-                    const float ex = __builtin_amdgcn_exp2f(-x * 1.44269504088896340736f);
-                    const float silu = x * __builtin_amdgcn_rcpf(1.0f + ex);
-                    if (gate_lane) hbuf[(32 * sl + acc_row(v)) * HS + col] = silu * y * wt[v];
+                    for (int v = 0; v < 16; ++v) {
+                        const float x = acc[j][q][v];
+                        const float y = dpp_move<0x128>(x);             // row_ror:8 = lane c ^ 8
+                        const float h = silu_up<FAST>(x, y, a.act_clamp) * wt[v];
+                        if (gate_lane) hbuf[(32 * sl + acc_row(v)) * HS + col] = h;
+                    }
                 }
             }
-        }
+        };
+        if (a.fast_math) write_h(IntTag<1>{});
+        else write_h(IntTag<0>{});
     });
 
     __syncthreads();
@@ -540,7 +561,7 @@ __device__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT>& lds, int e, int pb
 // L2 tile: pool rows [row0, row0 + valid) of expert e, W2 N block nb.
 // ---------------------------------------------------------------------------
 template <int MS, int BNT>
-__device__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT>& lds, int e, int pb, int row0,
+__device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT>& lds, int e, int pb, int row0,
                         int valid, int nb) {
     using C = Cfg<MS, BNT>;
     constexpr int BM = C::BM, BN = C::BN, NT = C::NT;

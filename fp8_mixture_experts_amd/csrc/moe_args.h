@@ -31,6 +31,8 @@ struct MoeArgs {
     uint32_t wait_spin_limit;  // bound on one L2 tile's wait for its L1 tiles
     int32_t n_xcd;      // accelerator complex dies (each with its own L2) of the device
     int32_t xcd_group;  // pool blocks per group of the N-major tile order
+    float act_clamp;    // clamp of gate and up before SiLU (+inf: none)
+    int32_t fast_math;  // 1: hardware exp2 and reciprocal in SiLU
 
     // inputs (caller-owned)
     const uint8_t* x;

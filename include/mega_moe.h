@@ -64,9 +64,11 @@ typedef struct mega_moe_config {
     int32_t intermediate;     /* I, multiple of 128 (W1 has 2*I rows)            */
     int32_t num_topk;         /* k, 1 <= k                                        */
     int32_t max_tokens;       /* largest T a forward call may pass, >= 0          */
-    float activation_clamp;   /* clamp of gate/up before SwiGLU (SM90 design 10.1
-                                 step 3); only +inf (no clamp) is supported       */
-    int32_t fast_math;        /* 0: accurate exp and division in SwiGLU (only 0) */
+    float activation_clamp;   /* > 0: gate and up are clamped to [-clamp, clamp]
+                                 before SwiGLU (SM90 design 10.1 step 3);
+                                 +inf: no clamp                                  */
+    int32_t fast_math;        /* 0: expf and IEEE division in SiLU; 1: hardware
+                                 exp2 and reciprocal (a few float32 ulps)        */
     int32_t block_m;          /* 0 = automatic (SM90 design 13.1), else 32/64/128 */
     int32_t l2_n_major;       /* -1 automatic (12.2), 0 M-major, 1 N-major L2 order */
     int32_t block_n;          /* output columns per expert-kernel tile: 0 = automatic,

@@ -58,6 +58,13 @@ def test_plan_matches_golden_tiers():
         assert p.l1_n_blocks == 2 * 2048 // p.block_n and p.l2_n_blocks == 7168 // p.block_n
 
 
+@pytest.mark.parametrize("kw", [dict(activation_clamp=10.0), dict(activation_clamp=0.25),
+                                dict(fast_math=1), dict(fast_math=1, activation_clamp=3.0)])
+def test_activation_options_are_accepted(kw):
+    assert B.mega_moe_workspace_bytes(_cfg(**kw)) > 0
+    B.mega_moe_plan(_cfg(**kw), 128)
+
+
 def test_plan_overrides():
     p = B.mega_moe_plan(_cfg(block_m=32, l2_n_major=1), 8192)
     assert p.block_m == 32 and p.l2_n_major == 1
@@ -73,7 +80,9 @@ def test_plan_overrides():
                                 dict(num_experts=0), dict(num_experts=5000), dict(max_tokens=-1),
                                 dict(block_m=48), dict(l2_n_major=2), dict(block_n=192),
                                 dict(block_m=32, block_n=256),
-                                dict(hidden=7296, block_n=256)])
+                                dict(hidden=7296, block_n=256), dict(activation_clamp=0.0),
+                                dict(activation_clamp=-1.0), dict(activation_clamp=math.nan),
+                                dict(fast_math=2)])
 def test_invalid_configs_are_rejected(kw):
     assert B.mega_moe_workspace_bytes(_cfg(**kw)) == -1
     with pytest.raises(B.MegaMoEError) as ei:
@@ -82,8 +91,7 @@ def test_invalid_configs_are_rejected(kw):
     assert B.mega_moe_last_error()
 
 
-@pytest.mark.parametrize("kw", [dict(activation_clamp=10.0), dict(fast_math=1),
-                                dict(hidden=8320), dict(intermediate=4224)])
+@pytest.mark.parametrize("kw", [dict(hidden=8320), dict(intermediate=8320)])
 def test_unbuilt_options_are_unsupported(kw):
     with pytest.raises(B.MegaMoEError) as ei:
         B.mega_moe_plan(_cfg(**kw), 1)

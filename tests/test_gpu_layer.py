@@ -7,6 +7,8 @@ Shapes span several tiles and ragged tails: pool blocks only partly filled,
 experts with several pool blocks, a single expert, top-1, inactive slots.
 """
 
+import math
+
 import numpy as np
 import pytest
 
@@ -64,6 +66,28 @@ def test_layer_matches_oracle(name):
         assert run.forward() == 0
         err = _compare_all(inp, ref, run, name)
         print(f"{name}: y rel frobenius {err:.2e}")
+    finally:
+        run.close()
+
+
+def _biting_clamp(inp):
+    """A clamp below about a third of the |gate| and |up| values of expert 0."""
+    acc = moe.l1_gemm(inp["x"][:8], inp["x_sf"][:8], inp["w1"][0], inp["w1_sf"][0])
+    return float(np.quantile(np.abs(acc), 0.7))
+
+
+@pytest.mark.parametrize("name", ["ragged", "skewed"])
+@pytest.mark.parametrize("fast_math", [0, 1])
+@pytest.mark.parametrize("clamped", [False, True])
+def test_activation_options_match_oracle(name, fast_math, clamped):
+    inp = S.make_inputs(SMALL[name])
+    clamp = _biting_clamp(inp) if clamped else math.inf
+    ref = moe.forward(inp, clamp=clamp)
+    run = G.Runner(inp, activation_clamp=clamp, fast_math=fast_math)
+    try:
+        assert run.forward() == 0
+        err = _compare_all(inp, ref, run, f"{name} clamp {clamp} fast_math {fast_math}")
+        print(f"{name} clamp {clamp:.4g} fast_math {fast_math}: y rel frobenius {err:.2e}")
     finally:
         run.close()
 
