@@ -27,7 +27,8 @@ MEGA_MOE_DEVERR_WAIT_TIMEOUT = 0x2
 
 EXPORTS = ["mega_moe_create", "mega_moe_forward", "mega_moe_destroy", "mega_moe_get_status",
            "mega_moe_last_error", "mega_moe_workspace_bytes", "mega_moe_token_alignment",
-           "mega_moe_plan", "mega_moe_get_views", "mega_moe_profile_begin",
+           "mega_moe_plan", "mega_moe_get_views", "mega_moe_set_recv_stats",
+           "mega_moe_transform_w1", "mega_moe_profile_begin",
            "mega_moe_profile_end"]
 
 
@@ -86,6 +87,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mega_moe_plan.restype = ctypes.c_int
     lib.mega_moe_get_views.argtypes = [vp, ctypes.POINTER(mega_moe_views)]
     lib.mega_moe_get_views.restype = ctypes.c_int
+    lib.mega_moe_transform_w1.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.mega_moe_transform_w1.restype = ctypes.c_int
+    lib.mega_moe_set_recv_stats.argtypes = [vp, vp]
+    lib.mega_moe_set_recv_stats.restype = ctypes.c_int
     lib.mega_moe_profile_begin.argtypes = [vp, i32]
     lib.mega_moe_profile_begin.restype = ctypes.c_int
     lib.mega_moe_profile_end.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32,
@@ -161,6 +166,18 @@ def mega_moe_get_views(handle) -> mega_moe_views:
     out = mega_moe_views()
     _check(load().mega_moe_get_views(handle, ctypes.byref(out)))
     return out
+
+
+def mega_moe_transform_w1(num_experts, hidden, intermediate, w1_plain, w1_sf_plain, w1_out,
+                          w1_sf_out, stream) -> int:
+    """Device pointers (ints); see include/mega_moe.h."""
+    return _check(load().mega_moe_transform_w1(num_experts, hidden, intermediate, w1_plain,
+                                               w1_sf_plain, w1_out, w1_sf_out, stream))
+
+
+def mega_moe_set_recv_stats(handle, stats) -> int:
+    """stats: device pointer of int32 [E] (or None to turn the statistics off)."""
+    return _check(load().mega_moe_set_recv_stats(handle, stats))
 
 
 def mega_moe_profile_begin(handle, max_calls: int) -> int:

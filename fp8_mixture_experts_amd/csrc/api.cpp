@@ -17,6 +17,8 @@ namespace mega_moe {
 void launch_dispatch(const MoeArgs& a, int gather_blocks, hipStream_t stream);
 int launch_expert_ffn(const MoeArgs& a, int num_cus, hipStream_t stream);
 void launch_combine(const MoeArgs& a, hipStream_t stream);
+void launch_transform_w1(const uint8_t* w1, const float* sf, uint8_t* out, float* out_sf, int E,
+                         int N, int H, hipStream_t stream);
 }  // namespace mega_moe
 
 using namespace mega_moe;
@@ -352,6 +354,35 @@ int mega_moe_get_status(mega_moe_handle* h, void* stream_v) {
     if (e != hipSuccess) return fail(MEGA_MOE_ERR_HIP, "status read: %s", hipGetErrorString(e));
     ok();
     return (int)bits;
+}
+
+int mega_moe_transform_w1(int32_t num_experts, int32_t hidden, int32_t intermediate,
+                          const uint8_t* w1_plain, const float* w1_sf_plain, uint8_t* w1_out,
+                          float* w1_sf_out, void* stream_v) {
+    if (num_experts < 1 || hidden <= 0 || hidden % 128 || intermediate <= 0 || intermediate % 128)
+        return fail(MEGA_MOE_ERR_INVALID_ARG,
+                    "need num_experts >= 1 and hidden, intermediate positive multiples of 128");
+    if (!w1_plain || !w1_sf_plain || !w1_out || !w1_sf_out)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned(w1_plain, 8) || !aligned(w1_out, 8) || !aligned(w1_sf_plain, 4) ||
+        !aligned(w1_sf_out, 4))
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "codes must be 8-byte and scales 4-byte aligned");
+    const size_t bytes = (size_t)num_experts * 2 * intermediate * hidden;
+    const uintptr_t a0 = (uintptr_t)w1_plain, b0 = (uintptr_t)w1_out;
+    if (a0 < b0 + bytes && b0 < a0 + bytes)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "w1_plain and w1_out overlap");
+    launch_transform_w1(w1_plain, w1_sf_plain, w1_out, w1_sf_out, num_experts, 2 * intermediate,
+                        hidden, (hipStream_t)stream_v);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MEGA_MOE_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int mega_moe_set_recv_stats(mega_moe_handle* h, int32_t* stats) {
+    if (!h) return fail(MEGA_MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (!aligned(stats, 4)) return fail(MEGA_MOE_ERR_INVALID_ARG, "stats must be 4-byte aligned");
+    h->base.recv_stats = stats;
+    return ok();
 }
 
 int mega_moe_profile_begin(mega_moe_handle* h, int32_t max_calls) {

@@ -84,6 +84,7 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
 }
 
 // With every expert's count in s_count (one workgroup of SCAN_THREADS):
+// the counts (also added to the caller's cumulative statistics when set),
 // 128-aligned segment offsets and pool blocks by a wavefront prefix scan over
 // the experts, the expert of every pool block with a cleared arrival counter,
 // each XCD's range of pool blocks, the cleared queue heads, and -1 in `src`
@@ -104,6 +105,7 @@ __device__ void finish_counts(const MoeArgs& a, const int* s_count, int* s_off, 
         s_off[e] = off;
         s_mb[e] = mb0;
         a.counts[e] = cnt;
+        if (a.recv_stats) a.recv_stats[e] += cnt;
         a.offsets[e] = off;
         a.mb_start[e] = mb0;
     }

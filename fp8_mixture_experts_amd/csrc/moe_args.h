@@ -61,6 +61,7 @@ struct MoeArgs {
     float* l2_sf;         // [I/64, P_cap]
     uint16_t* comb;       // [R, H]
     uint32_t* ready;      // [PB_cap] finished L1 tiles per pool block
+    int32_t* recv_stats;  // [E] caller-owned cumulative routes per expert, or null
     int32_t* xcd_info;    // [2 * MAX_XCD] first pool block and block count of each XCD
     MoeCtrl* ctrl;
 };

@@ -174,6 +174,35 @@ typedef struct mega_moe_views {
 int mega_moe_get_views(mega_moe_handle* h, mega_moe_views* out);
 
 /*
+ * Gate/up interleave of W1 for this layer (SM90 design 15.1), run once when
+ * the weights are loaded.  In: the plain W1 [E, 2I, H] E4M3 (all I gate rows,
+ * then all I up rows) and its float32 scales [E, 2I/128, H/128], one per
+ * 128x128 block of that tensor (finite, >= 0).  Out: the stored layout that
+ * mega_moe_forward takes (row 16g + r = gate row 8g + r for r < 8, up row
+ * 8g + r - 8 otherwise) and one scale per 128x128 block of it: the larger of
+ * the block's two source scales; the rows whose source scale is smaller are
+ * re-rounded to E4M3 (nearest, ties to even) at the ratio of the two, in
+ * float64; a block with both scales 0 gets scale 0 and codes 0.  H and I
+ * multiples of 128.  Device pointers owned by the caller; in and out must
+ * not overlap; 8-byte aligned codes, 4-byte aligned scales.  Asynchronous on
+ * `stream`; W2 needs no transform.
+ */
+int mega_moe_transform_w1(int32_t num_experts, int32_t hidden, int32_t intermediate,
+                          const uint8_t* w1_plain, const float* w1_sf_plain, uint8_t* w1_out,
+                          float* w1_sf_out, void* stream);
+
+/*
+ * Optional cumulative per-expert route counts (the cumulative local expert
+ * receive statistics of the pages' interface, SM90 design 16.1).  Once set,
+ * every forward call on the handle adds the number of routes each local
+ * expert received in that call to stats[e] (int32 [E], device memory owned
+ * by the caller, which zeroes it when it wants to start over), inside the
+ * dispatch on the call's stream.  NULL turns it off (the default).  The
+ * pointer must stay valid while forward calls that use it may run.
+ */
+int mega_moe_set_recv_stats(mega_moe_handle* h, int32_t* stats);
+
+/*
  * Optional timing of the three kernel groups of the next forward calls with
  * HIP events recorded on each call's stream (for benchmarks; the layer
  * computes the same thing with or without it).  profile_begin arms it for up

@@ -123,3 +123,13 @@ def test_create_without_gpu_fails_cleanly():
     with pytest.raises(B.MegaMoEError) as ei:
         B.mega_moe_create(_cfg())
     assert ei.value.code in (B.MEGA_MOE_ERR_HIP, B.MEGA_MOE_ERR_UNSUPPORTED)
+
+
+def test_transform_rejects_bad_arguments():
+    """Argument errors return before any HIP call, so no GPU is needed."""
+    with pytest.raises(B.MegaMoEError) as ei:
+        B.mega_moe_transform_w1(1, 100, 128, 16, 16, 16, 16, 0)
+    assert ei.value.code == B.MEGA_MOE_ERR_INVALID_ARG
+    with pytest.raises(B.MegaMoEError) as ei:                    # in and out overlap
+        B.mega_moe_transform_w1(1, 128, 128, 1 << 20, 1 << 12, (1 << 20) + 256, 1 << 13, 0)
+    assert ei.value.code == B.MEGA_MOE_ERR_INVALID_ARG

@@ -12,6 +12,7 @@ import math
 import numpy as np
 import pytest
 
+from fp8_mixture_experts_amd import binding as B
 from fp8_mixture_experts_amd import synthetic as S
 from oracle import moe
 from tests import gpu_util as G
@@ -176,6 +177,32 @@ def test_inactive_invalid_and_duplicate_slots():
         y = run.y()
         assert np.all(y[0] == 0)
         _compare_all(inp, ref, run, "edge slots")
+    finally:
+        run.close()
+
+
+def test_cumulative_recv_stats():
+    """Each forward adds its per-expert route counts to the caller's array;
+    None stops it."""
+    import torch
+    inp, ref = _case("skewed")
+    T = inp["x"].shape[0]
+    E = inp["w1"].shape[0]
+    half = moe.dispatch(inp["topk_idx"][: T // 2], E)["counts"]
+    run = G.Runner(inp)
+    try:
+        stats = torch.zeros(E, dtype=torch.int32, device="cuda")
+        B.mega_moe_set_recv_stats(run.layer.handle, stats.data_ptr())
+        assert run.forward() == 0
+        assert run.forward(num_tokens=T // 2) == 0
+        assert run.forward() == 0
+        torch.cuda.synchronize()
+        want = 2 * ref["counts"] + half
+        assert np.array_equal(stats.cpu().numpy(), want.astype(np.int32))
+        B.mega_moe_set_recv_stats(run.layer.handle, None)
+        assert run.forward() == 0
+        torch.cuda.synchronize()
+        assert np.array_equal(stats.cpu().numpy(), want.astype(np.int32))
     finally:
         run.close()
 
