@@ -159,6 +159,34 @@ def test_repeated_calls_are_bitwise_identical_and_leave_no_residue():
         run.close()
 
 
+EDGE = {
+    # the largest hidden and intermediate the library takes (64 K scale
+    # blocks per weight row block in LDS)
+    "max_dims": S.custom("max_dims", tokens=6, hidden=8192, intermediate=4096, experts=2,
+                         topk=2, seed=41, weight_seed=42),
+    "topk_all": S.custom("topk_all", tokens=20, hidden=256, intermediate=128, experts=4, topk=4,
+                         seed=43, weight_seed=44),
+    "one_expert_many_blocks": S.custom("one_expert_many_blocks", tokens=600, hidden=256,
+                                       intermediate=128, experts=1, topk=1, seed=45,
+                                       weight_seed=46),
+    "one_token": S.custom("one_token", tokens=1, hidden=512, intermediate=256, experts=8,
+                          topk=2, seed=47, weight_seed=48),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_shapes_match_oracle(name):
+    inp = S.make_inputs(EDGE[name])
+    ref = moe.forward(inp)
+    for bm in (0, 64, 128):
+        run = G.Runner(inp, block_m=bm)
+        try:
+            assert run.forward() == 0
+            _compare_all(inp, ref, run, f"{name} block_m {bm}")
+        finally:
+            run.close()
+
+
 def test_inactive_invalid_and_duplicate_slots():
     inp, _ = _case("ragged")
     inp = dict(inp)
