@@ -52,10 +52,14 @@
 // tiles each wave computes 2 slices x 2 column groups (a slice's A operand
 // and a group's B operand are then converted and read once for two output
 // blocks).  Each wave sums the whole K step of its blocks, so no partial sums
-// cross waves.  In L1 a column group's 32 stored W1 rows are four interleave
-// groups of 8 (gate, up, gate, up), so the gate and up values of an output
-// sit in lanes c and c+8 of one wave and meet through one DPP move.  32-row
-// slices that hold no routes are skipped.
+// cross waves.  The weights are the MFMA's A operand and the activations its
+// B operand, so a 32x32 result block is transposed: lane l holds activation
+// row l%32 and its register v weight row 8(v/4) + 4(l/32) + v%4.  A lane then
+// needs the scale of one activation row per block (one LDS read and one
+// multiply), and since a column group's 32 stored W1 rows are four interleave
+// groups of 8 (gate, up, gate, up), registers v and v + 4 of one lane hold
+// the gate and up values of the same output.  32-row slices that hold no
+// routes are skipped.
 #include <hip/hip_runtime.h>
 
 #include "moe_args.h"
@@ -177,6 +181,14 @@ __device__ __forceinline__ v16f row_vec(const float* base) {
     const float4 c = *reinterpret_cast<const float4*>(base + 16 + g4);
     const float4 d = *reinterpret_cast<const float4*>(base + 24 + g4);
     return v16f{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
+}
+
+// The scale of this lane's row of a 32-row slice (result blocks are
+// transposed: a lane holds one activation row), read as an
+// integer and reinterpreted for the same reason as stage_rows below.
+__device__ __forceinline__ float lane_row_scale(const uint8_t* sf_rows, int slice) {
+    const int r = 32 * slice + (threadIdx.x & 31);
+    return __builtin_bit_cast(float, *reinterpret_cast<const int*>(sf_rows + 4 * r));
 }
 
 // The per-row scales of a step, read from its stage in accumulator layout.
@@ -403,7 +415,6 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT>& ld
     const int H = a.H;
     const int KB = H / BK;
     const size_t P = a.P_cap;
-    const int c = threadIdx.x & 31;
     const int act = min(MS, (valid + 31) / 32);
 
     // the tile's NSB weight scale rows of W1_sf [E, 2I/128, H/128], contiguous
@@ -419,14 +430,11 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT>& ld
 
     const v16f zero = v16f{};
     // ---- epilogue buffer: h of the tile, written from the accumulators ----
-    // Lane c < 8 (mod 16) of a column group holds a gate value and lane c + 8
-    // the up value of the same output, 16g + 8*(c/16) + c%8 of the tile's
-    // BN/2 for column group g; one DPP rotation within each row of 16 lanes brings
-    // them together.  silu(g) = g / (1 + 2^(-g*log2 e)) with the hardware exp2
-    // and reciprocal (a few float32 ulps; the code rule tolerates them).  h
-    // goes to LDS; then one thread per 16 outputs of a row takes the row amax
-    // over its quad of threads (DPP), the exactly rounded scale amax / 448,
-    // and writes 16 codes (h * (1 / sf)) as one store.
+    // Each lane forms SwiGLU from a gate and an up accumulator it holds itself
+    // (the layout is spelled out at write_h below) and writes h to LDS; then
+    // one thread per 16 outputs of a row takes the row amax over its quad of
+    // threads (DPP), the exactly rounded scale amax / 448, and writes 16 codes
+    // (h * (1 / sf)) as one store.
     constexpr int HS = C::HS;                                           // h row stride (floats)
     float* hbuf = reinterpret_cast<float*>(lds.stage(0));              // [BM][HS]
 
@@ -459,15 +467,15 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT>& ld
                         const v8h a16 = f16_frag_part(stg, ly.s0 + j, p);
 #pragma unroll
                         for (int q = 0; q < LY::NG; ++q)
-                            d[j][q] = mfma_f16(a16, b16[q], p == 0 ? zero : d[j][q]);
+                            d[j][q] = mfma_f16(b16[q], a16, p == 0 ? zero : d[j][q]);
                     }
                 }
 #pragma unroll
                 for (int j = 0; j < LY::NJ; ++j) {
-                    const v16f svw = stage_rows(sfa + 128 * (ly.s0 + j)) * sw;
+                    const float svw = lane_row_scale(sfa, ly.s0 + j) * sw;
 #pragma unroll
                     for (int q = 0; q < LY::NG; ++q)
-                        acc[j][q] = __builtin_elementwise_fma(d[j][q], svw, acc[j][q]);
+                        acc[j][q] = __builtin_elementwise_fma(d[j][q], v16f(svw), acc[j][q]);
                 }
             } else {
                 // one column group: its B operand converted once per step,
@@ -479,32 +487,39 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT>& ld
 #pragma unroll
                 for (int j = 0; j < LY::NJ; ++j) {
                     const Frag fa = read_frag2(stg, j);
-                    const v16f sv = stage_rows(sfa + 128 * j);
-                    v16f d = mfma_f16(f16_part(fa.h[0], 0), b16[0], zero);
+                    const float svw = lane_row_scale(sfa, j) * sw;
+                    v16f d = mfma_f16(b16[0], f16_part(fa.h[0], 0), zero);
 #pragma unroll
-                    for (int p = 1; p < 8; ++p) d = mfma_f16(f16_part(fa.h[p >> 2], p & 3), b16[p], d);
-                    acc[j][0] = __builtin_elementwise_fma(d, sv * sw, acc[j][0]);
+                    for (int p = 1; p < 8; ++p) d = mfma_f16(b16[p], f16_part(fa.h[p >> 2], p & 3), d);
+                    acc[j][0] = __builtin_elementwise_fma(d, v16f(svw), acc[j][0]);
                 }
             }
         });
 
-        // the k loop ended with a barrier, so the stages are free for h
-        const bool gate_lane = (c & 8) == 0;
+        // the k loop ended with a barrier, so the stages are free for h.  In a
+        // transposed block, register v of lane l holds stored W1 row
+        // 8(v/4) + 4(l/32) + v%4 of the column group for activation row l%32:
+        // registers v and v + 4 (v%8 < 4) are the gate and up rows of output
+        // 16g + 8(v/8) + 4(l/32) + v%4, so SwiGLU needs no data from another
+        // lane, and each lane writes 4 consecutive outputs at a time.
         auto write_h = [&](auto fast) {
             constexpr bool FAST = decltype(fast)::value != 0;
 #pragma unroll
             for (int j = 0; j < LY::NJ; ++j) {
-                const int sl = ly.s0 + j;
-                const v16f wt = row_vec(lds.row_w() + 32 * sl);
+                const int row = 32 * (ly.s0 + j) + (threadIdx.x & 31);
+                const float wt = lds.row_w()[row];
 #pragma unroll
                 for (int q = 0; q < LY::NG; ++q) {
-                    const int col = 16 * (ly.g0 + q) + 8 * ((c >> 4) & 1) + (c & 7);
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const float x = acc[j][q][v];
-                        const float y = dpp_move<0x128>(x);             // row_ror:8 = lane c ^ 8
-                        const float h = silu_up<FAST>(x, y, a.act_clamp) * wt[v];
-                        if (gate_lane) hbuf[(32 * sl + acc_row(v)) * HS + col] = h;
+                    for (int half = 0; half < 2; ++half) {
+                        float hv[4];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            hv[v] = silu_up<FAST>(acc[j][q][8 * half + v], acc[j][q][8 * half + 4 + v],
+                                                  a.act_clamp) * wt;
+                        const int col = 16 * (ly.g0 + q) + 8 * half + 4 * ((threadIdx.x >> 5) & 1);
+                        *reinterpret_cast<float4*>(hbuf + row * HS + col) =
+                            float4{hv[0], hv[1], hv[2], hv[3]};
                     }
                 }
             }
@@ -568,7 +583,6 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT>& ld
     const int I = a.I;
     const int KB = I / BK;
     const size_t P = a.P_cap;
-    const int c = threadIdx.x & 31;
     const int act = min(MS, (valid + 31) / 32);
 
     // the tile's NSB weight scale rows of W2_sf [E, H/128, I/128], contiguous
@@ -618,25 +632,33 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT>& ld
                 const Frag fa = read_frag2(stg, sl);
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const v16f svw = stage_rows(sfa + 4 * (hh * BM + 32 * sl)) * sw;
+                    const float svw = lane_row_scale(sfa + 4 * hh * BM, sl) * sw;
 #pragma unroll
                     for (int q = 0; q < LY::NG; ++q) {
-                        const v16f d = mfma_f8(fa.h[hh], fb[q].h[hh], zero);
-                        acc[j][q] = __builtin_elementwise_fma(d, svw, acc[j][q]);
+                        const v16f d = mfma_f8(fb[q].h[hh], fa.h[hh], zero);
+                        acc[j][q] = __builtin_elementwise_fma(d, v16f(svw), acc[j][q]);
                     }
                 }
             }
         });
 
         // ---- epilogue: BF16 partials, staged so each route row is stored whole ----
+        // (transposed blocks: register v of lane l is column 8(v/4) + 4(l/32)
+        // + v%4 of the group for row l%32; four registers = 8 bytes of a row)
 #pragma unroll
-        for (int j = 0; j < LY::NJ; ++j)
+        for (int j = 0; j < LY::NJ; ++j) {
+            const int row = 32 * (ly.s0 + j) + (threadIdx.x & 31);
 #pragma unroll
             for (int q = 0; q < LY::NG; ++q)
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    stage[(32 * (ly.s0 + j) + acc_row(v)) * BN + 32 * (ly.g0 + q) + c] =
-                        bf16_rne(acc[j][q][v]);
+                for (int t = 0; t < 4; ++t) {
+                    const v16f& r = acc[j][q];
+                    const uint2 w2{(uint32_t)bf16_rne(r[4 * t]) | ((uint32_t)bf16_rne(r[4 * t + 1]) << 16),
+                                   (uint32_t)bf16_rne(r[4 * t + 2]) | ((uint32_t)bf16_rne(r[4 * t + 3]) << 16)};
+                    const int col = 32 * (ly.g0 + q) + 8 * t + 4 * ((threadIdx.x >> 5) & 1);
+                    *reinterpret_cast<uint2*>(stage + row * BN + col) = w2;
+                }
+        }
     });
     __syncthreads();
     for (int q = threadIdx.x; q < BM * (BN / 8); q += NT) {
