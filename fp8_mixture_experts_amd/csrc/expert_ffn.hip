@@ -150,19 +150,24 @@ __device__ __forceinline__ v8h f16_part(const v8i& f, int q) {
     return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// The same eight FP8 values read straight from the stage (one 8-byte LDS
-// read) and converted: part p of slice (or column group) s, p = 4h + q.
-__device__ __forceinline__ v8h f16_frag_part(const uint8_t* region, int s, int p) {
-    typedef int v2i __attribute__((ext_vector_type(2)));
+// The raw 16 bytes of parts 2m and 2m + 1 (p = 4h + q) of slice (or column
+// group) s: one LDS read.  K bytes 16m + [0,16) of the row for the lane's
+// half, in the chunk order read_frag uses.
+__device__ __forceinline__ v4i frag_pair_raw(const uint8_t* region, int s, int m) {
     const int L = threadIdx.x & 63;
     const int r = L & 31, g = L >> 5;
     const uint8_t* row = region + (32 * s + r) * 128;
-    const int chunk = (4 * (p >> 2) + 2 * ((p & 3) >> 1) + g) ^ row_swz(r);
-    const v2i d = *reinterpret_cast<const v2i*>(row + 16 * chunk + 8 * (p & 1));
-    const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[0], 1.0f, false);
-    const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[0], 1.0f, true);
-    const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[1], 1.0f, false);
-    const v2h e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[1], 1.0f, true);
+    const int chunk = (4 * (m >> 1) + 2 * (m & 1) + g) ^ row_swz(r);
+    return *reinterpret_cast<const v4i*>(row + 16 * chunk);
+}
+
+// Dwords 2h, 2h + 1 of a raw pair (part 2m + h) as one 16-K F16 operand.
+__device__ __forceinline__ v8h f16_of_pair(const v4i& raw, int h) {
+    const int d0 = raw[2 * h], d1 = raw[2 * h + 1];
+    const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
+    const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
+    const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
+    const v2h e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
     return v8h{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
 }
 
@@ -452,22 +457,36 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT>& ld
             const float sw = lds.w_sf()[ly.sblock() * KB + kb];
             const uint8_t* sfa = stg + C::A_BYTES + C::B_BYTES;
             if constexpr (LY::GRID) {
-                // eight 16-K parts; per part the B operands of the two column
-                // groups and the A operand of each slice are read and
-                // converted once and feed four independent MFMA chains
+                // eight 16-K parts in four pairs; the raw fragments of pair
+                // m + 1 (two column groups, two slices) are read while pair m
+                // is converted and fed to four independent MFMA chains, so
+                // the LDS latency overlaps the matrix work
+                static_assert(LY::NG + LY::NJ == 4, "2 x 2 wave blocks");
                 v16f d[LY::NJ][LY::NG];
+                v4i raw[2][4];
+                auto read_pair = [&](v4i* dst, int m) {
 #pragma unroll
-                for (int p = 0; p < 8; ++p) {
-                    v8h b16[LY::NG];
+                    for (int q = 0; q < LY::NG; ++q) dst[q] = frag_pair_raw(stg + C::A_BYTES, ly.g0 + q, m);
 #pragma unroll
-                    for (int q = 0; q < LY::NG; ++q)
-                        b16[q] = f16_frag_part(stg + C::A_BYTES, ly.g0 + q, p);
+                    for (int j = 0; j < LY::NJ; ++j) dst[LY::NG + j] = frag_pair_raw(stg, ly.s0 + j, m);
+                };
+                read_pair(raw[0], 0);
 #pragma unroll
-                    for (int j = 0; j < LY::NJ; ++j) {
-                        const v8h a16 = f16_frag_part(stg, ly.s0 + j, p);
+                for (int m = 0; m < 4; ++m) {
+                    if (m < 3) read_pair(raw[(m + 1) & 1], m + 1);
 #pragma unroll
-                        for (int q = 0; q < LY::NG; ++q)
-                            d[j][q] = mfma_f16(b16[q], a16, p == 0 ? zero : d[j][q]);
+                    for (int h = 0; h < 2; ++h) {
+                        const bool first = m == 0 && h == 0;
+                        v8h b16[LY::NG];
+#pragma unroll
+                        for (int q = 0; q < LY::NG; ++q) b16[q] = f16_of_pair(raw[m & 1][q], h);
+#pragma unroll
+                        for (int j = 0; j < LY::NJ; ++j) {
+                            const v8h a16 = f16_of_pair(raw[m & 1][LY::NG + j], h);
+#pragma unroll
+                            for (int q = 0; q < LY::NG; ++q)
+                                d[j][q] = mfma_f16(b16[q], a16, first ? zero : d[j][q]);
+                        }
                     }
                 }
 #pragma unroll
