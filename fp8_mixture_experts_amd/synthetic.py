@@ -24,6 +24,12 @@ Recipe:
 * W1 [E, 2I, H] (stored gate/up interleaved) and W2 [E, H, I]: float32
   N(0, 0.02^2), quantised per 128x128 block of the stored tensor by the same
   rule.  decode, mid and prefill share one weight set.
+* MXFP4 workloads (``*_mxfp4``) quantise the same float32 weights per row and
+  32 K elements instead: shared exponent X = floor(log2(amax)) - 2 (the OCP
+  MX rule for E2M1, whose largest exponent is 2), codes = E2M1 of w / 2^X
+  rounded to nearest, ties to even, saturating at 6, two codes per byte (the
+  first in the low nibble), scale byte X + 127.  PyTorch has no CPU cast to
+  FP4, so that rounding is written out below; it builds inputs only.
 * Routing: per token, k distinct experts by Gumbel-top-k on log expert weights
   (successive sampling without replacement).  Uniform: equal weights.  Zipf(s):
   a seeded permutation pi of the active experts, expert pi(r) weighted
@@ -58,6 +64,7 @@ class Workload:
     seed: int = 0                     # x / routing / logits streams
     weight_seed: int = 0              # weight stream (shared between workloads)
     weight_std: float = 0.02
+    weight_format: str = "fp8"        # "fp8" | "mxfp4"
 
 
 WORKLOADS = {
@@ -70,6 +77,9 @@ WORKLOADS = {
                         weight_seed=20261100),
     "wide": Workload("wide", 4096, 4096, 1536, 64, 2, seed=20261206, weight_seed=20261300),
 }
+for _n in ("tiny", "decode", "mid", "prefill"):
+    WORKLOADS[_n + "_mxfp4"] = dataclasses.replace(WORKLOADS[_n], name=_n + "_mxfp4",
+                                                   weight_format="mxfp4")
 
 
 def custom(name="custom", **kw) -> Workload:
@@ -94,6 +104,30 @@ def _quantize_blocks(v: torch.Tensor, rows: int, cols: int):
     return codes.numpy(), sf.reshape(*lead, R // rows, C // cols).numpy().astype(np.float32)
 
 
+# E2M1 magnitudes by code 0..7 and the midpoints between neighbours
+_E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+_E2M1_MID = (_E2M1_MAG[1:] + _E2M1_MAG[:-1]) / 2
+
+
+def _quantize_mxfp4(v: np.ndarray):
+    """float32 [R, C] -> (E2M1 pairs uint8 [R, C/2], UE8M0 uint8 [R, C/32])."""
+    R, C = v.shape
+    b = v.astype(np.float64).reshape(R, C // 32, 32)
+    amax = np.abs(b).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        x = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    x = np.clip(x, -127, 127).astype(np.int64)
+    q = b / np.ldexp(1.0, x)[..., None]
+    a = np.abs(q)
+    lo = np.searchsorted(_E2M1_MID, a, side="left")
+    tie = (lo < len(_E2M1_MID)) & (a == _E2M1_MID[np.minimum(lo, len(_E2M1_MID) - 1)])
+    code = np.where(tie & (lo % 2 == 1), lo + 1, lo).astype(np.uint8)   # ties to even
+    code |= np.where(np.signbit(q), 8, 0).astype(np.uint8)
+    code = code.reshape(R, C)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (x + 127).astype(np.uint8)
+
+
 def _gen_normal(seed_seq, shape, std):
     rng = np.random.Generator(np.random.PCG64(seed_seq))
     a = rng.standard_normal(shape, dtype=np.float32)
@@ -103,11 +137,13 @@ def _gen_normal(seed_seq, shape, std):
 
 
 def _weights_one_expert(args):
-    s1, s2, N, H, I, std = args
-    w1 = torch.from_numpy(_gen_normal(s1, (N, H), std))
-    w2 = torch.from_numpy(_gen_normal(s2, (H, I), std))
-    c1, f1 = _quantize_blocks(w1, 128, 128)
-    c2, f2 = _quantize_blocks(w2, 128, 128)
+    s1, s2, N, H, I, std, fmt = args
+    w1 = _gen_normal(s1, (N, H), std)
+    w2 = _gen_normal(s2, (H, I), std)
+    if fmt == "mxfp4":
+        return _quantize_mxfp4(w1) + _quantize_mxfp4(w2)
+    c1, f1 = _quantize_blocks(torch.from_numpy(w1), 128, 128)
+    c2, f2 = _quantize_blocks(torch.from_numpy(w2), 128, 128)
     return c1, f1, c2, f2
 
 
@@ -116,23 +152,34 @@ _WEIGHT_CACHE: dict = {}
 
 def make_weights(wl: Workload, threads: int | None = None):
     """Quantised expert weights of a workload (cached per process)."""
-    key = (wl.weight_seed, wl.experts, wl.hidden, wl.intermediate, wl.weight_std)
+    key = (wl.weight_seed, wl.experts, wl.hidden, wl.intermediate, wl.weight_std,
+           wl.weight_format)
     if key in _WEIGHT_CACHE:
         return _WEIGHT_CACHE[key]
     E, H, I = wl.experts, wl.hidden, wl.intermediate
     N = 2 * I
+    mx = wl.weight_format == "mxfp4"
+    if not mx and wl.weight_format != "fp8":
+        raise ValueError(wl.weight_format)
     kids = np.random.SeedSequence(wl.weight_seed).spawn(2 * E)
-    w1 = np.empty((E, N, H), np.uint8)
-    w1_sf = np.empty((E, N // 128, H // 128), np.float32)
-    w2 = np.empty((E, H, I), np.uint8)
-    w2_sf = np.empty((E, H // 128, I // 128), np.float32)
-    jobs = [(kids[2 * e], kids[2 * e + 1], N, H, I, wl.weight_std) for e in range(E)]
+    if mx:
+        shapes = [(N, H // 2), (N, H // 32), (H, I // 2), (H, I // 32)]
+        dtypes = [np.uint8] * 4
+        names = ["w1_fp4", "w1_e8", "w2_fp4", "w2_e8"]
+    else:
+        shapes = [(N, H), (N // 128, H // 128), (H, I), (H // 128, I // 128)]
+        dtypes = [np.uint8, np.float32, np.uint8, np.float32]
+        names = ["w1", "w1_sf", "w2", "w2_sf"]
+    arrs = [np.empty((E,) + sh, dt) for sh, dt in zip(shapes, dtypes)]
+    jobs = [(kids[2 * e], kids[2 * e + 1], N, H, I, wl.weight_std, wl.weight_format)
+            for e in range(E)]
     if threads is None:
         threads = min(16, max(1, len(_affinity())))
     with ThreadPoolExecutor(threads) as ex:
-        for e, (c1, f1, c2, f2) in enumerate(ex.map(_weights_one_expert, jobs)):
-            w1[e], w1_sf[e], w2[e], w2_sf[e] = c1, f1, c2, f2
-    out = dict(w1=w1, w1_sf=w1_sf, w2=w2, w2_sf=w2_sf)
+        for e, parts in enumerate(ex.map(_weights_one_expert, jobs)):
+            for arr, part in zip(arrs, parts):
+                arr[e] = part
+    out = dict(zip(names, arrs))
     _WEIGHT_CACHE[key] = out
     return out
 

@@ -12,12 +12,14 @@ The oracle is a plain, slow, float64 restatement of the layer that the page
 by the page "PR357 Green-Context Split MegaMoE code review" (cited as
 "PR357 review"):
 
-* ``codecs``  OCP FP8 E4M3 decode/encode (round-to-nearest-even, saturating)
-  and BF16 round-to-nearest-even.
+* ``codecs``  OCP FP8 E4M3 decode/encode (round-to-nearest-even, saturating),
+  BF16 round-to-nearest-even, and the MXFP4 weight format (E2M1 codes with
+  UE8M0 scales per 32 K elements) of the page's SM100 variant.
 * ``moe``     dispatch (counts, 128-aligned offsets, stable slot map, source
   metadata, pool copies), the L1 block-scaled GEMM, SwiGLU times the top-k
   weight, per-64 amax re-quantisation, the L2 block-scaled GEMM with per-64
-  activation scales, the BF16 partial cast and the FP32 top-k combine.
+  activation scales, the BF16 partial cast and the FP32 top-k combine; the
+  two GEMMs also for MXFP4 weights.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against something other
 than itself (exhaustive codec properties, a library cast, exact rational brute

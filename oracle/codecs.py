@@ -99,3 +99,63 @@ def bf16_to_f32(bits) -> np.ndarray:
 def f32(x) -> np.ndarray:
     """Round float64 values to float32 (IEEE round to nearest even)."""
     return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# MXFP4 weights ("SM90 design" §2.1 and §15.2: the SM100 kernel's weights are
+# FP4 E2M1 with UE8M0 scale factors, one per 32 K elements).  The formats are
+# those of the OCP microscaling (MX) specification: E2M1 is sign | 2 exponent
+# bits (bias 1) | 1 mantissa bit, no infinities or NaN, largest magnitude 6;
+# UE8M0 is an unsigned 8-bit power-of-two exponent with bias 127, 0xFF = NaN.
+# Two E2M1 codes share a byte, the first (even K) in the low nibble.
+# --------------------------------------------------------------------------
+
+MX_BLOCK = 32
+
+
+def _e2m1_value(code: int) -> float:
+    """Value of one E2M1 code by the format's definition."""
+    s = (code >> 3) & 1
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    if e == 0:
+        mag = m * 0.5                           # subnormal: 0.m x 2^(1-1)
+    else:
+        mag = (1.0 + m / 2.0) * 2.0 ** (e - 1)  # normal: 1.m x 2^(e-1)
+    return -mag if s else mag
+
+
+E2M1_TABLE = np.array([_e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """4-bit E2M1 codes (one per array element) -> float64 values (exact)."""
+    return E2M1_TABLE[np.asarray(codes, dtype=np.uint8) & 0xF]
+
+
+def unpack_e2m1(packed) -> np.ndarray:
+    """[..., K/2] bytes -> [..., K] codes: element 2i from the low nibble."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def ue8m0_decode(e) -> np.ndarray:
+    """UE8M0 exponent bytes -> float64 2^(e - 127); 0xFF is NaN."""
+    e = np.asarray(e, dtype=np.int64)
+    v = np.ldexp(1.0, e - 127)
+    return np.where(e == 0xFF, np.nan, v)
+
+
+def mxfp4_decode(packed, scales) -> np.ndarray:
+    """MXFP4 rows -> float64 values.
+
+    ``packed`` [..., K/2] E2M1 pairs, ``scales`` [..., K/32] UE8M0.  Element c
+    is e2m1(code c) * 2^(scales[c // 32] - 127), exact in float64 for every
+    code and scale.
+    """
+    v = e2m1_decode(unpack_e2m1(packed))
+    s = np.repeat(ue8m0_decode(scales), MX_BLOCK, axis=-1)
+    return v * s

@@ -35,7 +35,7 @@ import math
 import numpy as np
 
 from .codecs import (E4M3_MAX, bf16_rne, bf16_to_f32, e4m3_decode,
-                     e4m3_encode_rne, f32)
+                     e4m3_encode_rne, f32, mxfp4_decode)
 
 POOL_ALIGN = 128     # pool segment alignment = largest BLOCK_M ("SM90 design" §13.1)
 K_BLOCK = 128        # K granularity of activation and weight scales (§1.1, §15.2)
@@ -196,6 +196,55 @@ def l2_gemm(a_codes, a_sf64, w2_codes, w2_sf):
     return acc
 
 
+def l1_gemm_mx(a_codes, a_sf, w1_packed, w1_e8):
+    """L1 with MXFP4 weights: acc[r, n] = sum_kb a_sf[r, kb] * D_kb[r, n].
+
+    D_kb is the dot over K block kb of the decoded activations and the decoded
+    weights, each weight already carrying the UE8M0 scale of its 32-wide block
+    (the SM100 format, "SM90 design" §2.1, §15.2); the activations keep their
+    float32 per-128 scales.  A product of an E4M3 and a scaled E2M1 value is a
+    multiple of 2^(s-10) below 2^(s+12) for block exponent s, so the 128
+    products of D_kb lie on one grid of 2^(s_min-10) below 2^(s_max+19): D_kb
+    is exact in float64 whatever the summation order whenever the four block
+    exponents of a 128-wide K block differ by at most 24.  a_codes [m, H],
+    a_sf [m, H/128], w1_packed [N, H/2] E2M1 pairs, w1_e8 [N, H/32] UE8M0.
+    """
+    A = e4m3_decode(a_codes)
+    B = mxfp4_decode(w1_packed, w1_e8)
+    m, H = A.shape
+    acc = np.zeros((m, B.shape[0]), dtype=np.float64)
+    a_sf = np.asarray(a_sf, np.float64)
+    for kb in range(H // K_BLOCK):
+        ks = slice(kb * K_BLOCK, (kb + 1) * K_BLOCK)
+        acc += a_sf[:, kb][:, None] * (A[:, ks] @ B[:, ks].T)
+    return acc
+
+
+def l2_gemm_mx(a_codes, a_sf64, w2_packed, w2_e8):
+    """L2 with MXFP4 weights: acc[r, n] = sum_kb (s0 * D0 + s1 * D1).
+
+    D0, D1 are the dots over the two 64-wide halves of K block kb of the
+    decoded activations and the decoded, block-scaled weights (exact in
+    float64 when the two block exponents of a half differ by at most 25, by
+    the argument of ``l1_gemm_mx``); s0, s1 the per-64 activation scales.
+    There is no separate weight scale.  a_codes [m, I], a_sf64 [m, I/64],
+    w2_packed [H, I/2], w2_e8 [H, I/32].
+    """
+    A = e4m3_decode(a_codes)
+    B = mxfp4_decode(w2_packed, w2_e8)
+    m, I = A.shape
+    acc = np.zeros((m, B.shape[0]), dtype=np.float64)
+    s = np.asarray(a_sf64, np.float64)
+    for kb in range(I // K_BLOCK):
+        halves = []
+        for hh in range(2):
+            c0 = kb * K_BLOCK + hh * L2_SF_GROUP
+            ks = slice(c0, c0 + L2_SF_GROUP)
+            halves.append(s[:, 2 * kb + hh][:, None] * (A[:, ks] @ B[:, ks].T))
+        acc += halves[0] + halves[1]
+    return acc
+
+
 def expert_rows(a_codes, a_sf, topk_w, w1_codes, w1_sf, w2_codes, w2_sf, clamp=math.inf):
     """The whole per-route expert computation for some rows of one expert.
 
@@ -205,11 +254,40 @@ def expert_rows(a_codes, a_sf, topk_w, w1_codes, w1_sf, w2_codes, w2_sf, clamp=m
     ``part`` [m, H] uint16 BF16.
     """
     acc1 = l1_gemm(a_codes, a_sf, w1_codes, w1_sf)
+    return _rows_after_l1(acc1, topk_w, clamp,
+                          lambda codes, sf: l2_gemm(codes, sf, w2_codes, w2_sf))
+
+
+def expert_rows_mx(a_codes, a_sf, topk_w, w1_packed, w1_e8, w2_packed, w2_e8, clamp=math.inf):
+    """``expert_rows`` with MXFP4 weights (same outputs)."""
+    acc1 = l1_gemm_mx(a_codes, a_sf, w1_packed, w1_e8)
+    return _rows_after_l1(acc1, topk_w, clamp,
+                          lambda codes, sf: l2_gemm_mx(codes, sf, w2_packed, w2_e8))
+
+
+def _rows_after_l1(acc1, topk_w, clamp, l2):
     h = swiglu_weighted(acc1, topk_w, clamp)
     codes, sf = quantize_per64(h)
-    acc2 = l2_gemm(codes, sf.astype(np.float64), w2_codes, w2_sf)
+    acc2 = l2(codes, sf.astype(np.float64))
     part = bf16_rne(f32(acc2))
     return dict(l2_acts=codes, l2_acts_sf=sf, part=part)
+
+
+def _expert_fn(inp, clamp):
+    """(rows of expert e) -> expert_rows result, for either weight format.
+
+    MXFP4 inputs carry ``w1_fp4``, ``w1_e8``, ``w2_fp4``, ``w2_e8``; FP8 inputs
+    ``w1``, ``w1_sf``, ``w2``, ``w2_sf``.
+    """
+    if "w1_fp4" in inp:
+        return lambda e, a, a_sf, w: expert_rows_mx(a, a_sf, w, inp["w1_fp4"][e], inp["w1_e8"][e],
+                                                    inp["w2_fp4"][e], inp["w2_e8"][e], clamp)
+    return lambda e, a, a_sf, w: expert_rows(a, a_sf, w, inp["w1"][e], inp["w1_sf"][e],
+                                             inp["w2"][e], inp["w2_sf"][e], clamp)
+
+
+def _num_experts(inp):
+    return (inp["w1_fp4"] if "w1_fp4" in inp else inp["w1"]).shape[0]
 
 
 # --------------------------------------------------------------------------
@@ -240,17 +318,19 @@ def forward(inp, clamp=math.inf):
     """Full layer on one GPU's share: all routes local.
 
     ``inp`` holds x [T,H] uint8, x_sf [T,H/128] f32, topk_idx [T,k] int32,
-    topk_weights [T,k] f32, w1 [E,2I,H] uint8, w1_sf [E,2I/128,H/128] f32,
-    w2 [E,H,I] uint8, w2_sf [E,H/128,I/128] f32.  Returns every intermediate
-    the layer defines plus ``y`` [T,H] uint16 BF16.
+    topk_weights [T,k] f32 and either FP8 weights w1 [E,2I,H] uint8, w1_sf
+    [E,2I/128,H/128] f32, w2 [E,H,I] uint8, w2_sf [E,H/128,I/128] f32 or
+    MXFP4 weights w1_fp4 [E,2I,H/2], w1_e8 [E,2I,H/32], w2_fp4 [E,H,I/2],
+    w2_e8 [E,H,I/32] (uint8).  Returns every intermediate the layer defines
+    plus ``y`` [T,H] uint16 BF16.
     """
     x, x_sf = inp["x"], inp["x_sf"]
     topk_idx, topk_w = inp["topk_idx"], inp["topk_weights"]
-    w1, w1_sf, w2, w2_sf = inp["w1"], inp["w1_sf"], inp["w2"], inp["w2_sf"]
     T, H = x.shape
-    E, N, _ = w1.shape
-    I = N // 2
+    E = _num_experts(inp)
+    I = (inp["w2_fp4"].shape[2] * 2) if "w2_fp4" in inp else inp["w2"].shape[2]
     k = topk_idx.shape[1]
+    rows_of = _expert_fn(inp, clamp)
     disp = dispatch(topk_idx, E)
     pool = gather_pool(x, x_sf, topk_w, disp)
     P = disp["src"].shape[0]
@@ -262,8 +342,7 @@ def forward(inp, clamp=math.inf):
         if c == 0:
             continue
         rows = np.arange(disp["offsets"][e], disp["offsets"][e] + c)
-        out = expert_rows(pool["l1_acts"][rows], pool["l1_acts_sf"][:, rows].T,
-                          pool["l1_w"][rows], w1[e], w1_sf[e], w2[e], w2_sf[e], clamp)
+        out = rows_of(e, pool["l1_acts"][rows], pool["l1_acts_sf"][:, rows].T, pool["l1_w"][rows])
         l2_acts[rows] = out["l2_acts"]
         l2_acts_sf[:, rows] = out["l2_acts_sf"].T
         comb[disp["src"][rows]] = out["part"]
@@ -283,9 +362,10 @@ def forward_tokens(inp, tokens, clamp=math.inf):
     """
     x, x_sf = inp["x"], inp["x_sf"]
     topk_idx, topk_w = inp["topk_idx"], inp["topk_weights"]
-    E = inp["w1"].shape[0]
+    E = _num_experts(inp)
     k = topk_idx.shape[1]
     H = x.shape[1]
+    rows_of = _expert_fn(inp, clamp)
     work = {}
     for t in tokens:
         for j in range(k):
@@ -296,8 +376,7 @@ def forward_tokens(inp, tokens, clamp=math.inf):
     for e, lst in work.items():
         ts = np.array([t for t, _ in lst])
         js = np.array([j for _, j in lst])
-        out = expert_rows(x[ts], x_sf[ts], topk_w[ts, js], inp["w1"][e],
-                          inp["w1_sf"][e], inp["w2"][e], inp["w2_sf"][e], clamp)
+        out = rows_of(e, x[ts], x_sf[ts], topk_w[ts, js])
         for n, (t, j) in enumerate(lst):
             per_route[(t, j)] = {key: val[n] for key, val in out.items()}
     result = {}
