@@ -1,6 +1,7 @@
 """Benchmark of the fused FP8 MoE expert layer on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|mid|prefill|wide|tiny]
+                (any of decode, mid, prefill, tiny with the suffix _mxfp4: MXFP4 weights)
 
 A step is one forward of the whole layer (dispatch, the persistent expert
 kernel, combine) over one batch of seeded synthetic inputs already resident in
@@ -43,20 +44,24 @@ def work_of(inp):
     """Algorithmic work of one step (routing-dependent, exact for these inputs)."""
     x, idx = inp["x"], inp["topk_idx"]
     T, H = x.shape
-    E, N, _ = inp["w1"].shape
+    mx = "w1_fp4" in inp
+    E, N, _ = inp["w1_fp4" if mx else "w1"].shape
     I = N // 2
     k = idx.shape[1]
     act = (idx >= 0) & (idx < E)
     R = int(act.sum())
     active_experts = int(len(np.unique(idx[act])))
     flops = 6.0 * H * I * R
-    w_bytes = active_experts * (3.0 * H * I + 4.0 * (2 * I // 128) * (H // 128)
-                                + 4.0 * (H // 128) * (I // 128))
+    if mx:   # E2M1 pairs + one UE8M0 byte per 32 K of every row
+        w_bytes = active_experts * (3.0 * H * I / 2 + 3.0 * H * I / 32)
+    else:
+        w_bytes = active_experts * (3.0 * H * I + 4.0 * (2 * I // 128) * (H // 128)
+                                    + 4.0 * (H // 128) * (I // 128))
     io_bytes = T * H + 4.0 * T * (H // 128) + 8.0 * T * k + 2.0 * T * H
     # the expert kernel: weights + pool rows and scales in, re-quantised
     # activations out and back in, BF16 partials out
     route_bytes = H + 4.0 * (H // 128) + 4 + 2.0 * (I + 4.0 * (I // 64)) + 2.0 * H
-    return dict(T=T, H=H, I=I, E=E, k=k, R=R, active_experts=active_experts, flops=flops,
+    return dict(T=T, H=H, I=I, E=E, k=k, R=R, active_experts=active_experts, flops=flops, mx=mx,
                 weight_bytes=w_bytes, compulsory_bytes=w_bytes + io_bytes,
                 expert_kernel_bytes=w_bytes + R * route_bytes)
 
@@ -95,7 +100,7 @@ def cpu_baseline(name, inp, work):
         dt = time.perf_counter() - t0
         sample = f"first {n} of {T} tokens of the {name} workload, scaled by routes"
         frac = float(((inp["topk_idx"][:n] >= 0) & (inp["topk_idx"][:n] < work["E"])).sum()) / work["R"]
-    if name == "prefill":
+    if name.startswith("prefill"):
         value, unit = work["flops"] * frac / dt / 1e12, "TFLOP/s"
     else:
         value, unit = work["weight_bytes"] / (dt / frac) / 1e9, "GB/s"
@@ -130,17 +135,20 @@ def main():
     name = args.workload
     inp = S.make_inputs(name)
     work = work_of(inp)
+    wkeys = ("w1_fp4", "w1_e8", "w2_fp4", "w2_e8") if work["mx"] else ("w1", "w1_sf", "w2", "w2_sf")
     dev = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to("cuda:0")
-           for k in ("x", "x_sf", "topk_idx", "topk_weights", "w1", "w1_sf", "w2", "w2_sf")}
+           for k in ("x", "x_sf", "topk_idx", "topk_weights") + wkeys}
     T, H = inp["x"].shape
     y = torch.empty((T, H), dtype=torch.int16, device="cuda:0")
     layer = B.MegaMoE(work["E"], H, work["I"], work["k"], T, block_m=args.block_m,
                       block_n=args.block_n, l2_n_major=args.l2_n_major)
     plan = B.mega_moe_plan(layer.cfg, T)
 
+    fwd = layer.forward_mxfp4 if work["mx"] else layer.forward
+
     def step():
-        layer.forward(dev["x"], dev["x_sf"], dev["topk_idx"], dev["topk_weights"], dev["w1"],
-                      dev["w1_sf"], dev["w2"], dev["w2_sf"], y)
+        fwd(dev["x"], dev["x_sf"], dev["topk_idx"], dev["topk_weights"], dev[wkeys[0]],
+            dev[wkeys[1]], dev[wkeys[2]], dev[wkeys[3]], y)
 
     for _ in range(args.warmup):
         step()
@@ -182,7 +190,7 @@ def main():
     tflops = work["flops"] / s / 1e12
     wgbs = work["weight_bytes"] / s / 1e9
     t_roof = max(work["compulsory_bytes"] / (HBM_PEAK_GBS * 1e9), work["flops"] / (FP8_PEAK_TFLOPS * 1e12))
-    if name == "prefill":
+    if name.startswith("prefill"):
         value, unit = tflops, "TFLOP/s"
         roof = {"bound": "mfma", "achieved": work["flops"] / (expert_ms / 1e3) / 1e12,
                 "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
@@ -196,15 +204,18 @@ def main():
     roof["traffic"] = RS.read_traffic(
         os.path.join(ROOT, "profiles", f"moe_expert_ffn_{name}_hbm_traffic.txt"), name)
     roof["algorithmic_bytes"] = work["expert_kernel_bytes"]
-    roof["kernel"] = f"moe_expert_ffn<{plan.block_m}x{plan.block_n}>"
+    roof["kernel"] = (f"moe_expert_ffn<{plan.block_m}x128, mxfp4>" if work["mx"]
+                      else f"moe_expert_ffn<{plan.block_m}x{plan.block_n}>")
     roof["kernel_ms"] = expert_ms
     out = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "vs_baseline": None, "dtype": "fp8_e4m3 x mxfp4" if work["mx"] else "fp8_e4m3",
+        "data": "synthetic",
         "config": {"workload": name, "tokens": T, "hidden": H, "intermediate": work["I"],
                    "experts": work["E"], "topk": work["k"], "routing": inp["workload"].routing,
-                   "block_m": plan.block_m, "block_n": plan.block_n,
+                   "block_m": plan.block_m, "block_n": 128 if work["mx"] else plan.block_n,
+                   "weights": "mxfp4" if work["mx"] else "fp8",
                    "l2_n_major": plan.l2_n_major},
         "tflops": tflops, "weight_stream_gbs": wgbs,
         "pct_roofline": 100.0 * t_roof / s,

@@ -24,8 +24,10 @@ MEGA_MOE_ERR_OUT_OF_MEMORY = -4
 MEGA_MOE_ERR_DEVICE = -5
 MEGA_MOE_DEVERR_BAD_EXPERT = 0x1
 MEGA_MOE_DEVERR_WAIT_TIMEOUT = 0x2
+MEGA_MOE_DEVERR_SCALE_RANGE = 0x4
 
-EXPORTS = ["mega_moe_create", "mega_moe_forward", "mega_moe_destroy", "mega_moe_get_status",
+EXPORTS = ["mega_moe_create", "mega_moe_forward", "mega_moe_forward_mxfp4", "mega_moe_destroy",
+           "mega_moe_get_status",
            "mega_moe_last_error", "mega_moe_workspace_bytes", "mega_moe_token_alignment",
            "mega_moe_plan", "mega_moe_get_views", "mega_moe_set_recv_stats",
            "mega_moe_transform_w1", "mega_moe_profile_begin",
@@ -72,6 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mega_moe_create.restype = ctypes.c_int
     lib.mega_moe_forward.argtypes = [vp, i32] + [vp] * 9 + [vp]
     lib.mega_moe_forward.restype = ctypes.c_int
+    lib.mega_moe_forward_mxfp4.argtypes = [vp, i32] + [vp] * 9 + [vp]
+    lib.mega_moe_forward_mxfp4.restype = ctypes.c_int
     lib.mega_moe_destroy.argtypes = [vp]
     lib.mega_moe_destroy.restype = ctypes.c_int
     lib.mega_moe_get_status.argtypes = [vp, vp]
@@ -134,6 +138,15 @@ def mega_moe_forward(handle, num_tokens, x, x_sf, topk_idx, topk_weights, w1, w1
     return _check(load().mega_moe_forward(
         handle, num_tokens, ptr(x), ptr(x_sf), ptr(topk_idx), ptr(topk_weights), ptr(w1),
         ptr(w1_sf), ptr(w2), ptr(w2_sf), ptr(y), stream))
+
+
+def mega_moe_forward_mxfp4(handle, num_tokens, x, x_sf, topk_idx, topk_weights, w1, w1_scale,
+                           w2, w2_scale, y, stream) -> int:
+    """MXFP4 weights (E2M1 pairs + UE8M0 per 32 K); pointers as mega_moe_forward."""
+    ptr = lambda t: t if isinstance(t, int) else t.data_ptr()   # noqa: E731
+    return _check(load().mega_moe_forward_mxfp4(
+        handle, num_tokens, ptr(x), ptr(x_sf), ptr(topk_idx), ptr(topk_weights), ptr(w1),
+        ptr(w1_scale), ptr(w2), ptr(w2_scale), ptr(y), stream))
 
 
 def mega_moe_destroy(handle) -> int:
@@ -207,6 +220,14 @@ class MegaMoE:
             stream = torch.cuda.current_stream().cuda_stream
         return mega_moe_forward(self.handle, x.shape[0], x, x_sf, topk_idx, topk_weights, w1,
                                 w1_sf, w2, w2_sf, y, stream)
+
+    def forward_mxfp4(self, x, x_sf, topk_idx, topk_weights, w1, w1_scale, w2, w2_scale, y,
+                      stream=None):
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        return mega_moe_forward_mxfp4(self.handle, x.shape[0], x, x_sf, topk_idx, topk_weights,
+                                      w1, w1_scale, w2, w2_scale, y, stream)
 
     def status(self, stream=None) -> int:
         import torch

@@ -288,26 +288,46 @@ int mega_moe_destroy(mega_moe_handle* h) {
     return ok();
 }
 
-int mega_moe_forward(mega_moe_handle* h, int32_t T, const uint8_t* x, const float* x_sf,
-                     const int32_t* topk_idx, const float* topk_weights, const uint8_t* w1,
-                     const float* w1_sf, const uint8_t* w2, const float* w2_sf, uint16_t* y,
-                     void* stream_v) {
+// Weights of one forward call, in either format.
+struct WeightArgs {
+    int fmt;                      // W_FP8_ARGS or W_MXFP4_ARGS
+    const uint8_t* w1;
+    const float* w1_sf;
+    const uint8_t* w1_e8;
+    const uint8_t* w2;
+    const float* w2_sf;
+    const uint8_t* w2_e8;
+};
+constexpr int W_FP8_ARGS = 0, W_MXFP4_ARGS = 1;
+
+static int forward_impl(mega_moe_handle* h, int32_t T, const uint8_t* x, const float* x_sf,
+                        const int32_t* topk_idx, const float* topk_weights, const WeightArgs& w,
+                        uint16_t* y, void* stream_v) {
     if (!h) return fail(MEGA_MOE_ERR_INVALID_ARG, "handle is NULL");
     if (T < 0 || T > h->cfg.max_tokens)
         return fail(MEGA_MOE_ERR_INVALID_ARG, "num_tokens %d outside [0, max_tokens=%d]", T,
                     h->cfg.max_tokens);
     h->last_T = T;
     if (T == 0) return ok();
-    if (!x || !x_sf || !topk_idx || !topk_weights || !w1 || !w1_sf || !w2 || !w2_sf || !y)
+    const bool mx = w.fmt == W_MXFP4_ARGS;
+    const void* wsc1 = mx ? (const void*)w.w1_e8 : (const void*)w.w1_sf;
+    const void* wsc2 = mx ? (const void*)w.w2_e8 : (const void*)w.w2_sf;
+    if (!x || !x_sf || !topk_idx || !topk_weights || !w.w1 || !wsc1 || !w.w2 || !wsc2 || !y)
         return fail(MEGA_MOE_ERR_INVALID_ARG, "a tensor pointer is NULL");
-    if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(y, 16))
+    if (!aligned(x, 16) || !aligned(w.w1, 16) || !aligned(w.w2, 16) || !aligned(y, 16))
         return fail(MEGA_MOE_ERR_INVALID_ARG, "x, w1, w2 and y must be 16-byte aligned");
     if (!aligned(x_sf, 4) || !aligned(topk_idx, 4) || !aligned(topk_weights, 4) ||
-        !aligned(w1_sf, 4) || !aligned(w2_sf, 4))
+        !aligned(wsc1, 4) || !aligned(wsc2, 4))
         return fail(MEGA_MOE_ERR_INVALID_ARG, "scale, index and weight arrays must be 4-byte aligned");
     hipStream_t stream = (hipStream_t)stream_v;
     mega_moe_plan_info p;
     plan(h->cfg, T, &p);
+    if (mx) {
+        // MXFP4 weights run on 128-column tiles only
+        p.block_n = 128;
+        p.l1_n_blocks = 2 * h->cfg.intermediate / 128;
+        p.l2_n_blocks = h->cfg.hidden / 128;
+    }
     MoeArgs a = h->base;
     a.T = T;
     a.R = T * h->cfg.num_topk;
@@ -322,10 +342,13 @@ int mega_moe_forward(mega_moe_handle* h, int32_t T, const uint8_t* x, const floa
     a.x_sf = x_sf;
     a.topk_idx = topk_idx;
     a.topk_w = topk_weights;
-    a.w1 = w1;
-    a.w1_sf = w1_sf;
-    a.w2 = w2;
-    a.w2_sf = w2_sf;
+    a.w_fmt = mx ? 1 : 0;
+    a.w1 = w.w1;
+    a.w1_sf = w.w1_sf;
+    a.w1_e8 = w.w1_e8;
+    a.w2 = w.w2;
+    a.w2_sf = w.w2_sf;
+    a.w2_e8 = w.w2_e8;
     a.y = y;
     const int gather_blocks = a.R < 16384 ? a.R : 16384;
     const int call = h->prof_used < h->prof_max ? h->prof_used++ : -1;
@@ -339,6 +362,22 @@ int mega_moe_forward(mega_moe_handle* h, int32_t T, const uint8_t* x, const floa
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MEGA_MOE_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     return ok();
+}
+
+int mega_moe_forward(mega_moe_handle* h, int32_t T, const uint8_t* x, const float* x_sf,
+                     const int32_t* topk_idx, const float* topk_weights, const uint8_t* w1,
+                     const float* w1_sf, const uint8_t* w2, const float* w2_sf, uint16_t* y,
+                     void* stream_v) {
+    const WeightArgs w{W_FP8_ARGS, w1, w1_sf, nullptr, w2, w2_sf, nullptr};
+    return forward_impl(h, T, x, x_sf, topk_idx, topk_weights, w, y, stream_v);
+}
+
+int mega_moe_forward_mxfp4(mega_moe_handle* h, int32_t T, const uint8_t* x, const float* x_sf,
+                           const int32_t* topk_idx, const float* topk_weights, const uint8_t* w1,
+                           const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                           uint16_t* y, void* stream_v) {
+    const WeightArgs w{W_MXFP4_ARGS, w1, nullptr, w1_scale, w2, nullptr, w2_scale};
+    return forward_impl(h, T, x, x_sf, topk_idx, topk_weights, w, y, stream_v);
 }
 
 int mega_moe_get_status(mega_moe_handle* h, void* stream_v) {

@@ -37,6 +37,15 @@
 // L2 once per 64-K half (acc += (sa_half*sw) * D_half), as 5.3 and 5.4
 // describe.
 //
+// MXFP4 weights (the SM100 kernel's FP4 E2M1 codes with a UE8M0 scale per
+// 32 K, same page 2.1 and 15.2) run the same tiles from a second set of
+// instances: weight rows of 64 bytes per step plus the step's scale dword of
+// every row.  L1 converts the codes to F16 with the block scale folded in
+// (v_cvt_scalef32_pk_f16_fp4, exact for scales 2^-23 .. 2^13; others raise
+// MEGA_MOE_DEVERR_SCALE_RANGE) and keeps the exact F16 products; L2 feeds
+// the codes to the scaled MFMA with FP4 weights and FP8 activations, whose
+// per-lane E8M0 scale is exactly one 32-wide block of the lane's row.
+//
 // Memory pipeline.  A workgroup is 4 waves.  Each 128-K step of a tile is one
 // LDS stage: BLOCK_M activation rows and 128 weight rows of 128 bytes, then
 // the step's per-row activation scales.  Stages are filled by direct
@@ -75,12 +84,22 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int BK = 128;              // K bytes per step
+constexpr int BK = 128;              // K elements per step (bytes of an FP8 row)
 constexpr int MAX_W_SF = 64;         // K scale blocks of a weight row block (H/128, I/128 <= 64)
+constexpr int W_FP8 = 0;             // weight formats: FP8 E4M3 with float 128x128 block scales
+constexpr int W_MXFP4 = 1;           // FP4 E2M1 pairs with a UE8M0 scale per 32 K of a row
 
 __device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c) {
     // scale operands 0 select the plain (unscaled) FP8 x FP8 instruction
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// FP4 E2M1 weights (A: 32 values of one row, four dwords, the lane's 32-wide
+// K block) times FP8 activations (B), the A values scaled by 2^(scale_a - 127)
+// in the instruction (the lane's UE8M0 byte in bits 0..7).
+__device__ __forceinline__ v16f mfma_mx(const v4i& a, const v8i& b, const v16f& c, int scale_a) {
+    const v8i a8 = v8i{a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b, c, 4, 0, 0, scale_a, 0, 127);
 }
 
 __device__ __forceinline__ v16f mfma_f16(const v8h& a, const v8h& b, const v16f& c) {
@@ -110,8 +129,18 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, in
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)lds, 16, voff, soff, 0, AUX);
 }
 
+// The same with 4 bytes per lane: lane L writes lds + 4 L.
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)lds, 4, voff, soff, 0, 0);
+}
+
 // Row swizzle of the stage layout (see the header).
 __device__ __forceinline__ int row_swz(int n) { return (n & 7) ^ ((n >> 3) & 1); }
+
+// Chunk swizzle of the 64-byte MXFP4 weight rows of a stage: the 16-byte chunk
+// c of row n sits at position c ^ swz4(n), so the 8-byte part reads of 32
+// rows spread over the banks (two-way at most).
+__device__ __forceinline__ int swz4(int n) { return (n >> 1) & 3; }
 
 // ---------------------------------------------------------------------------
 // Operand fragments.  The MFMA operand of one 32-row (A) or 32-column (B)
@@ -169,6 +198,48 @@ __device__ __forceinline__ v8h f16_of_pair(const v4i& raw, int h) {
     const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
     const v2h e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
     return v8h{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
+}
+
+// MXFP4 weight rows in a stage: 64 bytes (128 E2M1 codes) per row.  The
+// 8 bytes that pair m (16-K parts 2m, 2m + 1) of lane half g needs: codes
+// K = 32m + 16g + [0, 16), the same K the FP8 activation parts carry.
+__device__ __forceinline__ uint2 fp4_pair_raw(const uint8_t* region, int s, int m) {
+    const int L = threadIdx.x & 63;
+    const int r = L & 31, g = L >> 5;
+    const uint8_t* row = region + (32 * s + r) * 64;
+    return *reinterpret_cast<const uint2*>(row + 16 * (m ^ swz4(r)) + 8 * g);
+}
+
+// 16 bytes (32 codes, K = 64hh + 32g + [0, 32)) of 64-K half hh for the
+// scaled FP4 x FP8 MFMA: one 32-wide K block, the lane's own scale block.
+__device__ __forceinline__ v4i fp4_half_raw(const uint8_t* region, int s, int hh) {
+    const int L = threadIdx.x & 63;
+    const int r = L & 31, g = L >> 5;
+    const uint8_t* row = region + (32 * s + r) * 64;
+    return *reinterpret_cast<const v4i*>(row + 16 * ((2 * hh + g) ^ swz4(r)));
+}
+
+// Eight E2M1 codes (one dword, low nibble first) times `scale` as one F16
+// operand.  Exact for scale = 2^x, -23 <= x <= 13 (every product is then an
+// F16 value, subnormals included).
+__device__ __forceinline__ v8h f16_of_fp4(uint32_t d, float scale) {
+    const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 0);
+    const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 1);
+    const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 2);
+    const v2h e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 3);
+    return v8h{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
+}
+
+// UE8M0 byte i of w as the float 2^(e - 127) (e = 0 gives 0, e = 255 infinity:
+// both fall outside the exact range and are reported).
+__device__ __forceinline__ float e8_scale(uint32_t w, int i) {
+    return __builtin_bit_cast(float, ((w >> (8 * i)) & 0xFFu) << 23);
+}
+
+// The scale dword (four UE8M0 bytes, the step's 32-K blocks) of stored weight
+// row 32 s + lane % 32, read as an integer like the fragments.
+__device__ __forceinline__ uint32_t lane_wsc(const uint8_t* wsc_rows, int s) {
+    return (uint32_t)*reinterpret_cast<const int*>(wsc_rows + 4 * (32 * s + (threadIdx.x & 31)));
 }
 
 // Accumulator layout of the 32x32 MFMA: register v of lane l holds row
@@ -245,102 +316,135 @@ __device__ __forceinline__ float dpp_move(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// One instance per tile shape: BLOCK_M = 32 MS pool rows x BN output columns
-// (128 or 256).  A tile has BN/32 waves, one per 32-column group.
-template <int MS, int BNT>
+// One instance per tile shape and weight format: BLOCK_M = 32 MS pool rows x
+// BN output columns (128 or 256; 128 for MXFP4 weights).  A tile has BN/32
+// waves, one per 32-column group.
+template <int MS, int BNT, int WF = W_FP8>
 struct Cfg {
+    static constexpr bool MX = WF == W_MXFP4;
     static constexpr int BM = 32 * MS;                    // pool rows per tile
     static constexpr int BN = BNT;                        // output columns per tile
     static constexpr int NW = BN / 32;                    // waves per workgroup
     static constexpr int NT = 64 * NW;                    // threads per workgroup
     static constexpr int NSB = BN / 128;                  // 128-row weight scale blocks per tile
+    static constexpr int B_ROW = MX ? BK / 2 : BK;        // weight bytes per row per step
     static constexpr int A_BYTES = BM * BK;               // activation rows of a stage
-    static constexpr int B_BYTES = BN * BK;               // weight rows of a stage
+    static constexpr int B_BYTES = BN * B_ROW;            // weight rows of a stage
+    static constexpr int WSC_BYTES = MX ? BN * 4 : 0;     // UE8M0 scales of the weight rows
     static constexpr int SF_BYTES = 2 * BM * 4;           // per-row scales of a step (2 halves in L2)
-    static constexpr int STAGE = A_BYTES + B_BYTES + SF_BYTES;
+    static constexpr int OFF_B = A_BYTES;
+    static constexpr int OFF_WSC = OFF_B + B_BYTES;
+    static constexpr int OFF_SF = OFF_WSC + WSC_BYTES;
+    static constexpr int STAGE = OFF_SF + SF_BYTES;
     // 128-column tiles: two workgroups share a CU (each SIMD runs one wave of
     // each) with half of the 160 KB of LDS each: 3 stages at 32- and 64-row
-    // tiles, 2 at 128-row tiles.  256-column tiles: one eight-wave workgroup
-    // per CU (two waves per SIMD) with 3 stages.  While one workgroup (or
-    // wave) fills or drains its pipeline at a tile boundary, or waits for an
-    // L1 tile, the other keeps loading.
+    // tiles, 2 at 128-row tiles (MXFP4 weights, half the bytes: 4 and 3).
+    // 256-column tiles: one eight-wave workgroup per CU (two waves per SIMD)
+    // with 3 stages.  While one workgroup (or wave) fills or drains its
+    // pipeline at a tile boundary, or waits for an L1 tile, the other keeps
+    // loading.
     static constexpr int WPC = BN == 128 ? 2 : 1;
-    static constexpr int S = BN == 128 && MS == 4 ? 2 : 3;
-    static constexpr int PT = (BM + BN) / (8 * NW);       // 1 KB row blocks per wave per step
-    static constexpr int A_J = BM / (8 * NW);             // of which activation rows
-    static constexpr int WAIT = (S - 2) * (PT + 1);       // loads younger than the current step
+    static constexpr int S = MX ? (MS == 4 ? 3 : 4) : (BN == 128 && MS == 4 ? 2 : 3);
+    static constexpr int A_BLK = A_BYTES / 1024;          // 1 KB load blocks of activation rows
+    static constexpr int B_BLK = B_BYTES / 1024;          // ... and of weight rows
+    static constexpr int B_RPB = 1024 / B_ROW;            // weight rows per block
+    static constexpr int PT = (A_BLK + B_BLK) / NW;       // 1 KB blocks per wave per step
+    static constexpr int A_J = A_BLK / NW;                // of which activation rows
+    static constexpr int LPS = PT + 1 + (MX ? 1 : 0);     // load instructions per wave per step
+    static constexpr int WAIT = (S - 2) * LPS;            // loads younger than the current step
     static constexpr int OFF_TILE = S * STAGE;            // per-tile area after the stages
     static constexpr int HS = BN / 2 + 4;                 // L1 epilogue h row stride (floats)
     static constexpr int LDS_BYTES = OFF_TILE + MAX_W_SF * NSB * 4 + BM * 4 + 16;
-    static_assert((BM + BN) % (8 * NW) == 0 && BM % (8 * NW) == 0, "row blocks per wave");
+    static_assert((A_BLK + B_BLK) % NW == 0 && A_BLK % NW == 0, "row blocks per wave");
+    static_assert(!MX || BN == 128, "MXFP4 weights use 128-column tiles");
     static_assert(WAIT < 64, "vmcnt range");
     static_assert(WPC * LDS_BYTES <= 160 * 1024, "LDS per CU");
     static_assert(BM * BN * 2 <= S * STAGE && BM * HS * 4 <= S * STAGE, "epilogue buffers");
 };
 
-template <int MS, int BNT>
+template <int MS, int BNT, int WF = W_FP8>
 struct Lds {
-    using C = Cfg<MS, BNT>;
+    using C = Cfg<MS, BNT, WF>;
     uint8_t* base;
     __device__ uint8_t* stage(int i) const { return base + i * C::STAGE; }
-    // weight scales of the tile: [NSB][KB]
+    // weight scales of the tile (FP8 weights): [NSB][KB]
     __device__ float* w_sf() const { return reinterpret_cast<float*>(base + C::OFF_TILE); }
     __device__ float* row_w() const { return w_sf() + MAX_W_SF * C::NSB; }   // top-k weight per row (L1)
     __device__ int* tile() const { return reinterpret_cast<int*>(row_w() + C::BM); }
 };
 
-// Issues the direct loads of one step.  Wave w fills the 1 KB row blocks
-// b = 4j + w (rows 8b..8b+7 of the stage: activation rows first, then weight
-// rows): lane q takes row 8b + q/8 and the chunk whose swizzled position is
-// q % 8.  Then each wave loads a quarter of the step's per-row scales (one
-// 64-row group of l1_sf, or the two 64-K halves of l2_sf, in the pool-minor
-// layout).  A step past the end (real = false) still issues the same number
-// of instructions, from lane 0 only, so every wave's count of outstanding
-// loads is the same at every step.
-template <int MS, int BNT, int HALVES>
+// Issues the direct loads of one step.  Wave w fills the 1 KB blocks
+// b = NW j + w of the stage: activation rows first (8 rows of 128 bytes per
+// block), then weight rows (8 FP8 rows of 128 bytes, or 16 MXFP4 rows of 64
+// bytes): lane q takes row q / (chunks per row) of its block and the chunk
+// whose swizzled position is q % (chunks per row).  Each wave then loads a
+// quarter of the step's per-row activation scales (one 64-row group of
+// l1_sf, or the two 64-K halves of l2_sf, in the pool-minor layout) and, with
+// MXFP4 weights, the UE8M0 dword (four 32-K blocks) of its 32 weight rows.
+// A step past the end (real = false) still issues the same number of
+// instructions, from lane 0 only, so every wave's count of outstanding loads
+// is the same at every step.
+template <int MS, int BNT, int HALVES, int WF = W_FP8>
 struct Loader {
-    using C = Cfg<MS, BNT>;
+    using C = Cfg<MS, BNT, WF>;
     // L2 tiles read the activations and scales their L1 tiles just wrote
     static constexpr int AUX_ACT = HALVES == 2 ? SC1 : 0;
     static constexpr int PT = C::PT;
     static constexpr int Q = 4 * HALVES * C::BM / C::NW;  // scale bytes per wave
-    __amdgpu_buffer_rsrc_t ra, rb, rs;
+    __amdgpu_buffer_rsrc_t ra, rb, rs, rw;
     int voff[PT];
     int sf_voff;
+    int wsc_voff;
     int w;
     int sf_step;     // bytes between the scale groups of consecutive steps
 
-    __device__ Loader(__amdgpu_buffer_rsrc_t ra_, __amdgpu_buffer_rsrc_t rb_, int row_bytes,
-                      __amdgpu_buffer_rsrc_t rs_, int P)
-        : ra(ra_), rb(rb_), rs(rs_) {
+    // ra: activation rows (row_a bytes each), rb: weight rows (row_b bytes),
+    // rs: activation scales (pool-minor, row stride P), rw: UE8M0 scale rows
+    // of the weight rows (row_w bytes; MXFP4 only)
+    __device__ Loader(__amdgpu_buffer_rsrc_t ra_, __amdgpu_buffer_rsrc_t rb_, int row_a, int row_b,
+                      __amdgpu_buffer_rsrc_t rs_, int P, __amdgpu_buffer_rsrc_t rw_, int row_w)
+        : ra(ra_), rb(rb_), rs(rs_), rw(rw_) {
         const int lane = threadIdx.x & 63;
         w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
         for (int j = 0; j < PT; ++j) {
-            const int n = 8 * (C::NW * j + w) + (lane >> 3);     // stage row
-            const int r = j < C::A_J ? n : n - C::BM;           // row of its operand
-            voff[j] = r * row_bytes + 16 * ((lane & 7) ^ row_swz(n));
+            const int b = C::NW * j + w;
+            if (j < C::A_J) {
+                const int n = 8 * b + (lane >> 3);                  // activation row
+                voff[j] = n * row_a + 16 * ((lane & 7) ^ row_swz(n));
+            } else if constexpr (C::MX) {
+                const int n = 16 * (b - C::A_BLK) + (lane >> 2);    // MXFP4 weight row
+                voff[j] = n * row_b + 16 * ((lane & 3) ^ swz4(n));
+            } else {
+                const int n = 8 * (b - C::A_BLK) + (lane >> 3);     // FP8 weight row
+                voff[j] = n * row_b + 16 * ((lane & 7) ^ row_swz(n));
+            }
         }
         // scale bytes [w*Q, w*Q + Q) of the step's 2*BM*4-byte scale area
         const int off = w * Q + 16 * lane;
         const int half = off / (C::BM * 4);
         sf_voff = half * P * 4 + (off - half * C::BM * 4);
         sf_step = HALVES * P * 4;
+        wsc_voff = (32 * w + (lane & 31)) * row_w;
     }
 
     __device__ __forceinline__ void issue(uint8_t* stage, int kb, bool real) const {
         const int lane = threadIdx.x & 63;
-        const int soff = real ? kb * BK : 0;
+        const int soff_a = real ? kb * BK : 0;
+        const int soff_b = real ? kb * C::B_ROW : 0;
 #pragma unroll
         for (int j = 0; j < PT; ++j) {
             if (real || lane == 0) {
-                if (j < C::A_J) dma16<AUX_ACT>(ra, stage + (C::NW * j + w) * 1024, voff[j], soff);
-                else dma16(rb, stage + (C::NW * j + w) * 1024, voff[j], soff);
+                if (j < C::A_J) dma16<AUX_ACT>(ra, stage + (C::NW * j + w) * 1024, voff[j], soff_a);
+                else dma16(rb, stage + (C::NW * j + w) * 1024, voff[j], soff_b);
             }
         }
         if (lane < Q / 16 && (real || lane == 0))
-            dma16<AUX_ACT>(rs, stage + C::A_BYTES + C::B_BYTES + w * Q, sf_voff,
-                  real ? kb * sf_step : 0);
+            dma16<AUX_ACT>(rs, stage + C::OFF_SF + w * Q, sf_voff, real ? kb * sf_step : 0);
+        if constexpr (C::MX) {
+            if (lane < 32 && (real || lane == 0))
+                dma4(rw, stage + C::OFF_WSC + 128 * w, wsc_voff, real ? kb * 4 : 0);
+        }
     }
 };
 
@@ -351,15 +455,16 @@ __device__ __forceinline__ void wait_barrier() {
 }
 
 // K loop over KB steps; compute(stage, kb) reads only stage.
-template <int MS, int BNT, int HALVES, typename Compute>
-__device__ __forceinline__ void k_loop(const Loader<MS, BNT, HALVES>& ld, const Lds<MS, BNT>& lds, int KB,
-                                       Compute&& compute) {
-    constexpr int S = Cfg<MS, BNT>::S;
+template <int MS, int BNT, int HALVES, int WF, typename Compute>
+__device__ __forceinline__ void k_loop(const Loader<MS, BNT, HALVES, WF>& ld, const Lds<MS, BNT, WF>& lds,
+                                       int KB, Compute&& compute) {
+    using C = Cfg<MS, BNT, WF>;
+    constexpr int S = C::S;
 #pragma unroll
     for (int d = 0; d < S - 1; ++d) ld.issue(lds.stage(d), d, d < KB);
     int cur = 0;
     for (int kb = 0; kb < KB; ++kb) {
-        wait_barrier<Cfg<MS, BNT>::WAIT>();
+        wait_barrier<C::WAIT>();
         const int nk = kb + S - 1;
         ld.issue(lds.stage(cur == 0 ? S - 1 : cur - 1), nk, nk < KB);
         compute(lds.stage(cur), kb);
@@ -412,26 +517,34 @@ __device__ __forceinline__ void dispatch_act(int act, Fn&& fn) {
 // ---------------------------------------------------------------------------
 // L1 tile: pool rows [row0, row0 + valid) of expert e, W1 N block nb.
 // ---------------------------------------------------------------------------
-template <int MS, int BNT>
-__device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT>& lds, int e, int pb, int row0,
-                        int valid, int nb) {
-    using C = Cfg<MS, BNT>;
+template <int MS, int BNT, int WF>
+__device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>& lds, int e, int pb,
+                                        int row0, int valid, int nb) {
+    using C = Cfg<MS, BNT, WF>;
     constexpr int BM = C::BM, BN = C::BN, NT = C::NT;
     const int H = a.H;
     const int KB = H / BK;
     const size_t P = a.P_cap;
     const int act = min(MS, (valid + 31) / 32);
+    const size_t wrow0 = (size_t)e * (2 * a.I) + (size_t)nb * BN;     // first stored W1 row
 
-    // the tile's NSB weight scale rows of W1_sf [E, 2I/128, H/128], contiguous
-    const float* wsf = a.w1_sf + ((size_t)e * a.nb1 + nb) * C::NSB * KB;
-    for (int i = threadIdx.x; i < C::NSB * KB; i += NT) lds.w_sf()[i] = wsf[i];
+    if constexpr (!C::MX) {
+        // the tile's NSB weight scale rows of W1_sf [E, 2I/128, H/128], contiguous
+        const float* wsf = a.w1_sf + ((size_t)e * a.nb1 + nb) * C::NSB * KB;
+        for (int i = threadIdx.x; i < C::NSB * KB; i += NT) lds.w_sf()[i] = wsf[i];
+    }
     for (int r = threadIdx.x; r < BM; r += NT) lds.row_w()[r] = a.l1_w[row0 + r];
     __syncthreads();
-    const Loader<MS, BNT, 1> ld(make_rsrc(a.l1_acts + (size_t)row0 * H, (uint32_t)valid * H),
-                           make_rsrc(a.w1 + ((size_t)e * (2 * a.I) + (size_t)nb * BN) * H,
-                                     (uint32_t)BN * H),
-                           H, make_rsrc(a.l1_sf + row0, (uint32_t)(((KB - 1) * P + BM) * 4)),
-                           (int)P);
+    const int row_b = C::MX ? H / 2 : H;
+    const Loader<MS, BNT, 1, WF> ld(
+        make_rsrc(a.l1_acts + (size_t)row0 * H, (uint32_t)valid * H),
+        make_rsrc(a.w1 + wrow0 * row_b, (uint32_t)(BN * row_b)), H, row_b,
+        make_rsrc(a.l1_sf + row0, (uint32_t)(((KB - 1) * P + BM) * 4)), (int)P,
+        make_rsrc(C::MX ? a.w1_e8 + wrow0 * (H / 32) : nullptr, C::MX ? (uint32_t)(BN * (H / 32)) : 0u),
+        H / 32);
+    // MXFP4: smallest and largest block scale this lane converted (reported
+    // when outside 2^-23 .. 2^13, where the F16 conversion stops being exact)
+    float sc_lo = 1.0f, sc_hi = 1.0f;
 
     const v16f zero = v16f{};
     // ---- epilogue buffer: h of the tile, written from the accumulators ----
@@ -453,9 +566,82 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT>& ld
 #pragma unroll
             for (int q = 0; q < LY::NG; ++q) acc[j][q] = v16f{};
 
-        k_loop<MS, BNT, 1>(ld, lds, KB, [&](const uint8_t* stg, int kb) {
+        k_loop(ld, lds, KB, [&](const uint8_t* stg, int kb) {
+            const uint8_t* sfa = stg + C::OFF_SF;
+            if constexpr (C::MX) {
+                // MXFP4 weights: each pair m of 16-K parts is one 32-K scale
+                // block; the codes convert to F16 with the block scale folded
+                // in, then the same F16 MFMA chains as FP8 weights
+                uint32_t wsc[LY::NG];
+#pragma unroll
+                for (int q = 0; q < LY::NG; ++q) wsc[q] = lane_wsc(stg + C::OFF_WSC, ly.g0 + q);
+                v16f d[LY::NJ][LY::NG];
+                if constexpr (LY::GRID) {
+                    uint2 rb[2][LY::NG];
+                    v4i ra[2][LY::NJ];
+                    auto read_pair = [&](int buf, int m) {
+#pragma unroll
+                        for (int q = 0; q < LY::NG; ++q) rb[buf][q] = fp4_pair_raw(stg + C::OFF_B, ly.g0 + q, m);
+#pragma unroll
+                        for (int j = 0; j < LY::NJ; ++j) ra[buf][j] = frag_pair_raw(stg, ly.s0 + j, m);
+                    };
+                    read_pair(0, 0);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        if (m < 3) read_pair((m + 1) & 1, m + 1);
+                        float sc[LY::NG];
+#pragma unroll
+                        for (int q = 0; q < LY::NG; ++q) {
+                            sc[q] = e8_scale(wsc[q], m);
+                            sc_lo = fminf(sc_lo, sc[q]);
+                            sc_hi = fmaxf(sc_hi, sc[q]);
+                        }
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const bool first = m == 0 && h == 0;
+                            v8h b16[LY::NG];
+#pragma unroll
+                            for (int q = 0; q < LY::NG; ++q)
+                                b16[q] = f16_of_fp4(h ? rb[m & 1][q].y : rb[m & 1][q].x, sc[q]);
+#pragma unroll
+                            for (int j = 0; j < LY::NJ; ++j) {
+                                const v8h a16 = f16_of_pair(ra[m & 1][j], h);
+#pragma unroll
+                                for (int q = 0; q < LY::NG; ++q)
+                                    d[j][q] = mfma_f16(b16[q], a16, first ? zero : d[j][q]);
+                            }
+                        }
+                    }
+                } else {
+                    v8h b16[8];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const uint2 raw = fp4_pair_raw(stg + C::OFF_B, ly.g0, m);
+                        const float sc = e8_scale(wsc[0], m);
+                        sc_lo = fminf(sc_lo, sc);
+                        sc_hi = fmaxf(sc_hi, sc);
+                        b16[2 * m] = f16_of_fp4(raw.x, sc);
+                        b16[2 * m + 1] = f16_of_fp4(raw.y, sc);
+                    }
+#pragma unroll
+                    for (int j = 0; j < LY::NJ; ++j) {
+                        const Frag fa = read_frag2(stg, j);
+                        d[j][0] = mfma_f16(b16[0], f16_part(fa.h[0], 0), zero);
+#pragma unroll
+                        for (int p = 1; p < 8; ++p) d[j][0] = mfma_f16(b16[p], f16_part(fa.h[p >> 2], p & 3), d[j][0]);
+                    }
+                }
+                // no weight scale left to apply: promote by the row's x_sf
+#pragma unroll
+                for (int j = 0; j < LY::NJ; ++j) {
+                    const float sa = lane_row_scale(sfa, ly.s0 + j);
+#pragma unroll
+                    for (int q = 0; q < LY::NG; ++q)
+                        acc[j][q] = __builtin_elementwise_fma(d[j][q], v16f(sa), acc[j][q]);
+                }
+                return;
+            }
             const float sw = lds.w_sf()[ly.sblock() * KB + kb];
-            const uint8_t* sfa = stg + C::A_BYTES + C::B_BYTES;
             if constexpr (LY::GRID) {
                 // eight 16-K parts in four pairs; the raw fragments of pair
                 // m + 1 (two column groups, two slices) are read while pair m
@@ -466,7 +652,7 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT>& ld
                 v4i raw[2][4];
                 auto read_pair = [&](v4i* dst, int m) {
 #pragma unroll
-                    for (int q = 0; q < LY::NG; ++q) dst[q] = frag_pair_raw(stg + C::A_BYTES, ly.g0 + q, m);
+                    for (int q = 0; q < LY::NG; ++q) dst[q] = frag_pair_raw(stg + C::OFF_B, ly.g0 + q, m);
 #pragma unroll
                     for (int j = 0; j < LY::NJ; ++j) dst[LY::NG + j] = frag_pair_raw(stg, ly.s0 + j, m);
                 };
@@ -499,7 +685,7 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT>& ld
             } else {
                 // one column group: its B operand converted once per step,
                 // then one MFMA chain per active slice
-                const Frag fb = read_frag2(stg + C::A_BYTES, ly.g0);
+                const Frag fb = read_frag2(stg + C::OFF_B, ly.g0);
                 v8h b16[8];
 #pragma unroll
                 for (int p = 0; p < 8; ++p) b16[p] = f16_part(fb.h[p >> 2], p & 3);
@@ -546,6 +732,10 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT>& ld
         if (a.fast_math) write_h(IntTag<1>{});
         else write_h(IntTag<0>{});
     });
+    if constexpr (C::MX) {
+        if (!(sc_lo >= 0x1p-23f && sc_hi <= 0x1p13f))
+            atomicOr(&a.ctrl->error, MEGA_MOE_DEVERR_SCALE_RANGE);
+    }
 
     __syncthreads();
     // BN/32 threads per row, 16 outputs each; the 4 of one 64-output scale
@@ -594,19 +784,22 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT>& ld
 // ---------------------------------------------------------------------------
 // L2 tile: pool rows [row0, row0 + valid) of expert e, W2 N block nb.
 // ---------------------------------------------------------------------------
-template <int MS, int BNT>
-__device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT>& lds, int e, int pb, int row0,
-                        int valid, int nb) {
-    using C = Cfg<MS, BNT>;
+template <int MS, int BNT, int WF>
+__device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>& lds, int e, int pb,
+                                        int row0, int valid, int nb) {
+    using C = Cfg<MS, BNT, WF>;
     constexpr int BM = C::BM, BN = C::BN, NT = C::NT;
     const int I = a.I;
     const int KB = I / BK;
     const size_t P = a.P_cap;
     const int act = min(MS, (valid + 31) / 32);
 
-    // the tile's NSB weight scale rows of W2_sf [E, H/128, I/128], contiguous
-    const float* wsf = a.w2_sf + ((size_t)e * a.nb2 + nb) * C::NSB * KB;
-    for (int i = threadIdx.x; i < C::NSB * KB; i += NT) lds.w_sf()[i] = wsf[i];
+    const size_t wrow0 = (size_t)e * a.H + (size_t)nb * BN;         // first W2 row
+    if constexpr (!C::MX) {
+        // the tile's NSB weight scale rows of W2_sf [E, H/128, I/128], contiguous
+        const float* wsf = a.w2_sf + ((size_t)e * a.nb2 + nb) * C::NSB * KB;
+        for (int i = threadIdx.x; i < C::NSB * KB; i += NT) lds.w_sf()[i] = wsf[i];
+    }
     // wait until every L1 tile of this pool block has published
     if (threadIdx.x == 0) {
         uint32_t spins = 0;
@@ -621,10 +814,13 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT>& ld
     }
     __syncthreads();
 
-    const Loader<MS, BNT, 2> ld(make_rsrc(a.l2_acts + (size_t)row0 * I, (uint32_t)valid * I),
-                           make_rsrc(a.w2 + ((size_t)e * a.H + (size_t)nb * BN) * I, (uint32_t)BN * I),
-                           I, make_rsrc(a.l2_sf + row0, (uint32_t)(((2 * KB - 1) * P + BM) * 4)),
-                           (int)P);
+    const int row_b = C::MX ? I / 2 : I;
+    const Loader<MS, BNT, 2, WF> ld(
+        make_rsrc(a.l2_acts + (size_t)row0 * I, (uint32_t)valid * I),
+        make_rsrc(a.w2 + wrow0 * row_b, (uint32_t)(BN * row_b)), I, row_b,
+        make_rsrc(a.l2_sf + row0, (uint32_t)(((2 * KB - 1) * P + BM) * 4)), (int)P,
+        make_rsrc(C::MX ? a.w2_e8 + wrow0 * (I / 32) : nullptr, C::MX ? (uint32_t)(BN * (I / 32)) : 0u),
+        I / 32);
 
     const v16f zero = v16f{};
     uint16_t* stage = reinterpret_cast<uint16_t*>(lds.stage(0));  // BF16 [BM][BN] after the k loop
@@ -639,12 +835,41 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT>& ld
 #pragma unroll
             for (int q = 0; q < LY::NG; ++q) acc[j][q] = v16f{};
 
-        k_loop<MS, BNT, 2>(ld, lds, KB, [&](const uint8_t* stg, int kb) {
+        k_loop(ld, lds, KB, [&](const uint8_t* stg, int kb) {
+            const uint8_t* sfa = stg + C::OFF_SF;
+            if constexpr (C::MX) {
+                // MXFP4 weights: the scaled MFMA applies each lane's 32-K block
+                // scale (lane half g of 64-K half hh holds block 2hh + g)
+                const int g = (threadIdx.x >> 5) & 1;
+                uint32_t wsc[LY::NG];
+                v4i fb[LY::NG][2];
+#pragma unroll
+                for (int q = 0; q < LY::NG; ++q) {
+                    wsc[q] = lane_wsc(stg + C::OFF_WSC, ly.g0 + q);
+                    fb[q][0] = fp4_half_raw(stg + C::OFF_B, ly.g0 + q, 0);
+                    fb[q][1] = fp4_half_raw(stg + C::OFF_B, ly.g0 + q, 1);
+                }
+#pragma unroll
+                for (int j = 0; j < LY::NJ; ++j) {
+                    const int sl = ly.s0 + j;
+                    const Frag fa = read_frag2(stg, sl);
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const float sa = lane_row_scale(sfa + 4 * hh * BM, sl);
+#pragma unroll
+                        for (int q = 0; q < LY::NG; ++q) {
+                            const int e8 = (int)((wsc[q] >> (8 * (2 * hh + g))) & 0xFFu);
+                            const v16f d = mfma_mx(fb[q][hh], fa.h[hh], zero, e8);
+                            acc[j][q] = __builtin_elementwise_fma(d, v16f(sa), acc[j][q]);
+                        }
+                    }
+                }
+                return;
+            }
             const float sw = lds.w_sf()[ly.sblock() * KB + kb];
-            const uint8_t* sfa = stg + C::A_BYTES + C::B_BYTES;
             Frag fb[LY::NG];
 #pragma unroll
-            for (int q = 0; q < LY::NG; ++q) fb[q] = read_frag2(stg + C::A_BYTES, ly.g0 + q);
+            for (int q = 0; q < LY::NG; ++q) fb[q] = read_frag2(stg + C::OFF_B, ly.g0 + q);
 #pragma unroll
             for (int j = 0; j < LY::NJ; ++j) {
                 const int sl = ly.s0 + j;
@@ -712,12 +937,12 @@ __device__ __forceinline__ void tile_coords(int u, int cnt, int nbs, int G, bool
 // Two workgroups of four waves per CU, one wave of each per SIMD; the launch
 // puts num_cus * 2 of them in flight and they take tiles until their XCD's
 // queue is empty.
-template <int MS, int BNT>
-__global__ void __launch_bounds__((Cfg<MS, BNT>::NT)) __attribute__((amdgpu_waves_per_eu(2)))
+template <int MS, int BNT, int WF>
+__global__ void __launch_bounds__((Cfg<MS, BNT, WF>::NT)) __attribute__((amdgpu_waves_per_eu(2)))
 moe_expert_ffn(MoeArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg<MS, BNT>::LDS_BYTES];
-    const Lds<MS, BNT> lds{smem};
-    constexpr int BM = Cfg<MS, BNT>::BM;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg<MS, BNT, WF>::LDS_BYTES];
+    const Lds<MS, BNT, WF> lds{smem};
+    constexpr int BM = Cfg<MS, BNT, WF>::BM;
     // XCC_ID hardware register, bits [3:0]
     const int xcd = (__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xf) % a.n_xcd;
     const int G = a.xcd_group;
@@ -739,28 +964,35 @@ moe_expert_ffn(MoeArgs a) {
         const int m_local = pb - __builtin_amdgcn_readfirstlane(a.mb_start[e]);
         const int row0 = __builtin_amdgcn_readfirstlane(a.offsets[e]) + m_local * BM;
         const int valid = min(BM, __builtin_amdgcn_readfirstlane(a.counts[e]) - m_local * BM);
-        if (is_l1) l1_tile<MS, BNT>(a, lds, e, pb, row0, valid, nb);
-        else l2_tile<MS, BNT>(a, lds, e, pb, row0, valid, nb);
+        if (is_l1) l1_tile(a, lds, e, pb, row0, valid, nb);
+        else l2_tile(a, lds, e, pb, row0, valid, nb);
         __syncthreads();
     }
 }
 
-template <int MS, int BNT>
+template <int MS, int BNT, int WF = W_FP8>
 static int launch_one(const MoeArgs& a, int num_cus, hipStream_t stream) {
-    constexpr int NT = Cfg<MS, BNT>::NT;
+    constexpr int NT = Cfg<MS, BNT, WF>::NT;
     static int per_cu = 0;   // occupancy of this instance (same on every call)
     if (per_cu == 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_expert_ffn<MS, BNT>, NT, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_expert_ffn<MS, BNT, WF>, NT, 0) !=
                 hipSuccess || n < 1)
             n = 1;
         per_cu = n;
     }
-    hipLaunchKernelGGL((moe_expert_ffn<MS, BNT>), dim3(num_cus * per_cu), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((moe_expert_ffn<MS, BNT, WF>), dim3(num_cus * per_cu), dim3(NT), 0, stream, a);
     return num_cus * per_cu;
 }
 
 int launch_expert_ffn(const MoeArgs& a, int num_cus, hipStream_t stream) {
+    if (a.w_fmt == W_MXFP4) {
+        switch (a.block_m) {
+            case 32: return launch_one<1, 128, W_MXFP4>(a, num_cus, stream);
+            case 64: return launch_one<2, 128, W_MXFP4>(a, num_cus, stream);
+            default: return launch_one<4, 128, W_MXFP4>(a, num_cus, stream);
+        }
+    }
     if (a.block_n == 256) {
         if (a.block_m == 64) return launch_one<2, 256>(a, num_cus, stream);
         return launch_one<4, 256>(a, num_cus, stream);

@@ -33,16 +33,19 @@ struct MoeArgs {
     int32_t xcd_group;  // pool blocks per group of the N-major tile order
     float act_clamp;    // clamp of gate and up before SiLU (+inf: none)
     int32_t fast_math;  // 1: hardware exp2 and reciprocal in SiLU
+    int32_t w_fmt;      // 0: FP8 weights with float block scales, 1: MXFP4 weights
 
     // inputs (caller-owned)
     const uint8_t* x;
     const float* x_sf;
     const int32_t* topk_idx;
     const float* topk_w;
-    const uint8_t* w1;
-    const float* w1_sf;
-    const uint8_t* w2;
-    const float* w2_sf;
+    const uint8_t* w1;      // FP8 [E, 2I, H] or E2M1 pairs [E, 2I, H/2]
+    const float* w1_sf;     // FP8: [E, 2I/128, H/128]
+    const uint8_t* w1_e8;   // MXFP4: UE8M0 [E, 2I, H/32]
+    const uint8_t* w2;      // FP8 [E, H, I] or E2M1 pairs [E, H, I/2]
+    const float* w2_sf;     // FP8: [E, H/128, I/128]
+    const uint8_t* w2_e8;   // MXFP4: UE8M0 [E, H, I/32]
     uint16_t* y;
 
     // workspace (handle-owned)

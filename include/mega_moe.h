@@ -53,6 +53,7 @@ typedef enum mega_moe_status {
 /* Device error bits reported by mega_moe_get_status (sticky until read). */
 #define MEGA_MOE_DEVERR_BAD_EXPERT 0x1u   /* a topk_idx >= num_experts (route skipped) */
 #define MEGA_MOE_DEVERR_WAIT_TIMEOUT 0x2u /* an L2 tile gave up waiting for its L1 tiles */
+#define MEGA_MOE_DEVERR_SCALE_RANGE 0x4u  /* an MXFP4 W1 block scale outside 2^-23..2^13 */
 
 /*
  * Layer configuration (SM90 design 16.1: the expert count, top-k, the
@@ -114,6 +115,30 @@ int mega_moe_forward(mega_moe_handle* h, int32_t num_tokens,
                      const uint8_t* w1, const float* w1_sf,
                      const uint8_t* w2, const float* w2_sf,
                      uint16_t* y, void* stream);
+
+/*
+ * mega_moe_forward with MXFP4 weights: the FP4 E2M1 weights with UE8M0 scale
+ * factors, one per 32 K elements, of the SM100 kernel (SM90 design 2.1 and
+ * 15.2); activations, routing and output as in mega_moe_forward.
+ *   w1        [E, 2I, H/2]  uint8, two E2M1 codes per byte, the even K in the
+ *                           low nibble; rows gate/up interleaved by 8 as in
+ *                           mega_moe_forward
+ *   w1_scale  [E, 2I, H/32] uint8 UE8M0: element c of row n is
+ *                           e2m1(code) * 2^(w1_scale[n][c/32] - 127)
+ *   w2        [E, H, I/2]   uint8, E2M1 pairs
+ *   w2_scale  [E, H, I/32]  uint8 UE8M0
+ * The L1 product is exact (F16 matrix cores on the scaled codes) when every
+ * w1_scale lies in [104, 140] (block scales 2^-23 .. 2^13); a block outside
+ * that range sets MEGA_MOE_DEVERR_SCALE_RANGE and the rows of its tile are
+ * unspecified.  w2_scale may be any finite exponent (0..254).  The tiles are
+ * 128 columns wide whatever cfg.block_n says.  Errors as mega_moe_forward.
+ */
+int mega_moe_forward_mxfp4(mega_moe_handle* h, int32_t num_tokens,
+                           const uint8_t* x, const float* x_sf,
+                           const int32_t* topk_idx, const float* topk_weights,
+                           const uint8_t* w1, const uint8_t* w1_scale,
+                           const uint8_t* w2, const uint8_t* w2_scale,
+                           uint16_t* y, void* stream);
 
 /* Frees the workspace and the handle; NULL is accepted. */
 int mega_moe_destroy(mega_moe_handle* h);

@@ -42,9 +42,28 @@ def d2h(ptr: int, shape, dtype) -> np.ndarray:
     return out
 
 
+FP8_WEIGHTS = ("w1", "w1_sf", "w2", "w2_sf")
+MXFP4_WEIGHTS = ("w1_fp4", "w1_e8", "w2_fp4", "w2_e8")
+
+
+def is_mxfp4(inp):
+    return "w1_fp4" in inp
+
+
+def layer_dims(inp):
+    """(E, H, I, k) of an input set of either weight format."""
+    k = inp["topk_idx"].shape[1]
+    if is_mxfp4(inp):
+        E, N, _ = inp["w1_fp4"].shape
+    else:
+        E, N, _ = inp["w1"].shape
+    return E, inp["x"].shape[1], N // 2, k
+
+
 def to_device(inp, dev="cuda:0"):
     t = {}
-    for key in ("x", "x_sf", "topk_idx", "topk_weights", "w1", "w1_sf", "w2", "w2_sf"):
+    weights = MXFP4_WEIGHTS if is_mxfp4(inp) else FP8_WEIGHTS
+    for key in ("x", "x_sf", "topk_idx", "topk_weights") + weights:
         t[key] = torch.from_numpy(np.ascontiguousarray(inp[key])).to(dev)
     T, H = inp["x"].shape
     t["y"] = torch.empty((T, H), dtype=torch.int16, device=dev)
@@ -55,20 +74,25 @@ class Runner:
     """One layer handle sized for a workload; runs forwards and reads views."""
 
     def __init__(self, inp, max_tokens=None, **cfg):
-        E, N, H = inp["w1"].shape
-        k = inp["topk_idx"].shape[1]
+        E, H, I, k = layer_dims(inp)
         T = inp["x"].shape[0]
-        self.E, self.H, self.I, self.k = E, H, N // 2, k
-        self.layer = B.MegaMoE(E, H, N // 2, k, max_tokens if max_tokens is not None else T, **cfg)
+        self.E, self.H, self.I, self.k = E, H, I, k
+        self.mx = is_mxfp4(inp)
+        self.layer = B.MegaMoE(E, H, I, k, max_tokens if max_tokens is not None else T, **cfg)
         self.dev = to_device(inp)
 
     def forward(self, dev=None, num_tokens=None):
         d = dev or self.dev
         T = d["x"].shape[0] if num_tokens is None else num_tokens
         stream = torch.cuda.current_stream().cuda_stream
-        B.mega_moe_forward(self.layer.handle, T, d["x"], d["x_sf"], d["topk_idx"],
-                           d["topk_weights"], d["w1"], d["w1_sf"], d["w2"], d["w2_sf"], d["y"],
-                           stream)
+        if self.mx:
+            B.mega_moe_forward_mxfp4(self.layer.handle, T, d["x"], d["x_sf"], d["topk_idx"],
+                                     d["topk_weights"], d["w1_fp4"], d["w1_e8"], d["w2_fp4"],
+                                     d["w2_e8"], d["y"], stream)
+        else:
+            B.mega_moe_forward(self.layer.handle, T, d["x"], d["x_sf"], d["topk_idx"],
+                               d["topk_weights"], d["w1"], d["w1_sf"], d["w2"], d["w2_sf"],
+                               d["y"], stream)
         status = self.layer.status()
         return status
 

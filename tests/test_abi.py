@@ -114,6 +114,9 @@ def test_forward_rejects_bad_calls_without_touching_the_gpu():
     with pytest.raises(B.MegaMoEError) as ei:
         B.mega_moe_forward(None, 4, *([0] * 9), None)
     assert ei.value.code == B.MEGA_MOE_ERR_INVALID_ARG
+    with pytest.raises(B.MegaMoEError) as ei:
+        B.mega_moe_forward_mxfp4(None, 4, *([0] * 9), None)
+    assert ei.value.code == B.MEGA_MOE_ERR_INVALID_ARG
 
 
 def test_create_without_gpu_fails_cleanly():
