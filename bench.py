@@ -117,6 +117,9 @@ def main():
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--block-n", type=int, default=0)
     ap.add_argument("--l2-n-major", type=int, default=-1)
+    ap.add_argument("--split-l2-cus", type=int, default=0,
+                    help="run L1 and L2 tiles as two concurrent kernels, the L2 one with this "
+                         "many CUs' worth of workgroups per XCD (0: one fused kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
@@ -141,7 +144,8 @@ def main():
     T, H = inp["x"].shape
     y = torch.empty((T, H), dtype=torch.int16, device="cuda:0")
     layer = B.MegaMoE(work["E"], H, work["I"], work["k"], T, block_m=args.block_m,
-                      block_n=args.block_n, l2_n_major=args.l2_n_major)
+                      block_n=args.block_n, l2_n_major=args.l2_n_major,
+                      split_l2_cus=args.split_l2_cus)
     plan = B.mega_moe_plan(layer.cfg, T)
 
     fwd = layer.forward_mxfp4 if work["mx"] else layer.forward
@@ -216,6 +220,7 @@ def main():
                    "experts": work["E"], "topk": work["k"], "routing": inp["workload"].routing,
                    "block_m": plan.block_m, "block_n": 128 if work["mx"] else plan.block_n,
                    "weights": "mxfp4" if work["mx"] else "fp8",
+                   "split_l2_cus": args.split_l2_cus,
                    "l2_n_major": plan.l2_n_major},
         "tflops": tflops, "weight_stream_gbs": wgbs,
         "pct_roofline": 100.0 * t_roof / s,

@@ -96,6 +96,9 @@ int check_config(const mega_moe_config* c) {
     if (c->block_n == 256 && !wide_tiles_fit(*c))
         return fail(MEGA_MOE_ERR_INVALID_ARG,
                     "block_n 256 needs 2*intermediate and hidden multiples of 256 and block_m != 32");
+    if (c->split_l2_cus < 0 || c->split_l2_cus > 31)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "split_l2_cus must be in [0, 31], got %d",
+                    c->split_l2_cus);
     return MEGA_MOE_OK;
 }
 
@@ -174,6 +177,11 @@ struct mega_moe_handle {
     // optional event timing of the kernel groups (4 events per call)
     std::vector<hipEvent_t> prof_events;
     int32_t prof_max = 0, prof_used = 0;
+    // split phases: streams of the L1 and L2 kernels, the CUs' worth of
+    // workgroups each gets, and the fork / join events
+    hipStream_t split_stream[2] = {nullptr, nullptr};
+    int split_cus[2] = {0, 0};
+    hipEvent_t split_event[3] = {nullptr, nullptr, nullptr};
 };
 
 namespace {
@@ -186,6 +194,42 @@ void prof_release(mega_moe_handle* h) {
 hipEvent_t prof_event(mega_moe_handle* h, int call, int which) {
     if (call < 0) return nullptr;
     return h->prof_events[(size_t)call * 4 + which];
+}
+
+void split_release(mega_moe_handle* h) {
+    for (hipStream_t& st : h->split_stream)
+        if (st) { hipStreamDestroy(st); st = nullptr; }
+    for (hipEvent_t& ev : h->split_event)
+        if (ev) { hipEventDestroy(ev); ev = nullptr; }
+    h->split_cus[0] = h->split_cus[1] = 0;
+}
+
+// Sets up the split phases: two streams of their own for the L1 and L2
+// kernels, forked from and joined into the caller's stream with events.  The
+// two kernels get disjoint workgroup budgets that together fill the device
+// (two workgroups per CU): `l2` CUs' worth per XCD for the L2 kernel, the rest
+// for L1, so both are resident together whichever starts first.  Both grids
+// are multiples of the XCD count, and workgroups are dealt to the XCDs in
+// turn, so every XCD runs workgroups of both kernels and each takes only its
+// own XCD's tiles, as in the fused kernel.
+int split_setup(mega_moe_handle* h, int l2) {
+    const int nx = h->base.n_xcd;
+    const int per_xcd = h->num_cus / nx;
+    if (l2 >= per_xcd)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "split_l2_cus %d leaves no L1 CU on an XCD of %d CUs", l2,
+                    per_xcd);
+    h->split_cus[0] = (per_xcd - l2) * nx;
+    h->split_cus[1] = l2 * nx;
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < 2 && e == hipSuccess; ++i)
+        e = hipStreamCreateWithFlags(&h->split_stream[i], hipStreamNonBlocking);
+    for (int i = 0; i < 3 && e == hipSuccess; ++i)
+        e = hipEventCreateWithFlags(&h->split_event[i], hipEventDisableTiming);
+    if (e != hipSuccess) {
+        split_release(h);
+        return fail(MEGA_MOE_ERR_HIP, "split streams: %s", hipGetErrorString(e));
+    }
+    return MEGA_MOE_OK;
 }
 }  // namespace
 
@@ -250,7 +294,7 @@ int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out) {
     a.E = cfg->num_experts;
     a.k = cfg->num_topk;
     a.P_cap = L.P_cap;
-    a.wait_spin_limit = 1u << 22;
+    a.wait_spin_limit = 1u << 20;
     a.act_clamp = cfg->activation_clamp;
     a.fast_math = cfg->fast_math;
     // gfx950 groups 32 compute units per XCD, each XCD with its own L2
@@ -275,6 +319,15 @@ int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out) {
     a.xcd_info = (int32_t*)(w + L.off[L_XCDINFO]);
     a.ctrl = (MoeCtrl*)(w + L.off[L_CTRL]);
     h->last_T = 0;
+    if (cfg->split_l2_cus > 0) {
+        rc = split_setup(h, cfg->split_l2_cus);
+        if (rc) {
+            const std::string msg = g_last_error;
+            hipFree(h->ws);
+            delete h;
+            return fail(rc, "%s", msg.c_str());
+        }
+    }
     *out = h;
     return ok();
 }
@@ -282,6 +335,7 @@ int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out) {
 int mega_moe_destroy(mega_moe_handle* h) {
     if (!h) return ok();
     prof_release(h);
+    split_release(h);
     hipError_t e = hipFree(h->ws);
     delete h;
     if (e != hipSuccess) return fail(MEGA_MOE_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
@@ -355,7 +409,22 @@ static int forward_impl(mega_moe_handle* h, int32_t T, const uint8_t* x, const f
     if (call >= 0) hipEventRecord(prof_event(h, call, 0), stream);
     launch_dispatch(a, gather_blocks, stream);
     if (call >= 0) hipEventRecord(prof_event(h, call, 1), stream);
-    launch_expert_ffn(a, h->num_cus, stream);
+    if (h->split_stream[0]) {
+        // the L1 and L2 tiles as two concurrent kernels on disjoint CU sets,
+        // forked from and joined back into the caller's stream
+        hipEventRecord(h->split_event[0], stream);
+        for (int i = 0; i < 2; ++i) {
+            hipStreamWaitEvent(h->split_stream[i], h->split_event[0], 0);
+            MoeArgs ai = a;
+            ai.phase = i + 1;
+            launch_expert_ffn(ai, h->split_cus[i], h->split_stream[i]);
+            hipEventRecord(h->split_event[1 + i], h->split_stream[i]);
+        }
+        hipStreamWaitEvent(stream, h->split_event[1], 0);
+        hipStreamWaitEvent(stream, h->split_event[2], 0);
+    } else {
+        launch_expert_ffn(a, h->num_cus, stream);
+    }
     if (call >= 0) hipEventRecord(prof_event(h, call, 2), stream);
     launch_combine(a, stream);
     if (call >= 0) hipEventRecord(prof_event(h, call, 3), stream);

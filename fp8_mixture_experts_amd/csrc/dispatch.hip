@@ -115,7 +115,10 @@ __device__ void finish_counts(const MoeArgs& a, const int* s_count, int* s_off, 
         a.offsets[E] = total_rows;
         a.mb_start[E] = total_mb;
         a.ctrl->total_mb = total_mb;
-        for (int x = 0; x < MAX_XCD; ++x) a.ctrl->next_tile[x] = 0;
+        for (int x = 0; x < MAX_XCD; ++x) {
+            a.ctrl->next_tile[x] = 0;
+            a.ctrl->next_tile_l2[x] = 0;
+        }
     }
     __syncthreads();
 

@@ -949,12 +949,17 @@ moe_expert_ffn(MoeArgs a) {
     const int first = a.xcd_info[2 * xcd], cnt = a.xcd_info[2 * xcd + 1];
     const int l1_tiles = cnt * a.nb1;
     const int total = l1_tiles + cnt * a.nb2;
+    // phase 0: one queue, L1 tiles then L2 tiles; phase 1: the L1 tiles of that
+    // queue only; phase 2: the L2 tiles, from a queue of their own
+    const int end = a.phase == 1 ? l1_tiles : total;
     for (;;) {
-        if (threadIdx.x == 0) *lds.tile() = atomicAdd(&a.ctrl->next_tile[xcd], 1);
+        if (threadIdx.x == 0)
+            *lds.tile() = a.phase == 2 ? l1_tiles + atomicAdd(&a.ctrl->next_tile_l2[xcd], 1)
+                                       : atomicAdd(&a.ctrl->next_tile[xcd], 1);
         __syncthreads();
         const int u = __builtin_amdgcn_readfirstlane(*lds.tile());
         __syncthreads();
-        if (u >= total) break;
+        if (u >= end) break;
         const bool is_l1 = u < l1_tiles;
         int j, nb;
         if (is_l1) tile_coords(u, cnt, a.nb1, G, a.n_major, j, nb);

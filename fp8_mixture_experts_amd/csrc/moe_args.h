@@ -11,9 +11,11 @@ constexpr int MAX_XCD = 16;
 
 // Control record in device memory, reset by the dispatch scan of every call.
 struct MoeCtrl {
-    int32_t next_tile[MAX_XCD];  // work queue head of each XCD's tiles
-    int32_t total_mb;            // number of pool blocks (BLOCK_M rows) over all experts
-    uint32_t error;              // sticky MEGA_MOE_DEVERR_* bits
+    int32_t next_tile[MAX_XCD];     // work queue head of each XCD's tiles (L1 tiles only
+                                    // when the phases run as two kernels)
+    int32_t next_tile_l2[MAX_XCD];  // each XCD's L2 tile queue when they do
+    int32_t total_mb;               // number of pool blocks (BLOCK_M rows) over all experts
+    uint32_t error;                 // sticky MEGA_MOE_DEVERR_* bits
     int32_t pad[2];
 };
 
@@ -34,6 +36,7 @@ struct MoeArgs {
     float act_clamp;    // clamp of gate and up before SiLU (+inf: none)
     int32_t fast_math;  // 1: hardware exp2 and reciprocal in SiLU
     int32_t w_fmt;      // 0: FP8 weights with float block scales, 1: MXFP4 weights
+    int32_t phase;      // expert kernel: 0 L1 and L2 tiles, 1 L1 tiles only, 2 L2 tiles only
 
     // inputs (caller-owned)
     const uint8_t* x;

@@ -75,6 +75,12 @@ typedef struct mega_moe_config {
     int32_t block_n;          /* output columns per expert-kernel tile: 0 = automatic,
                                  128, or 256 (needs 2I % 256 == 0, H % 256 == 0 and
                                  block_m != 32) */
+    int32_t split_l2_cus;     /* 0: one persistent kernel takes the L1 and L2 tiles.
+                                 n > 0: the L1 and L2 tiles run as two concurrent
+                                 kernels on streams of their own (the green-context
+                                 split of the PR357 review, sections 1 and 5.2): the
+                                 L2 kernel gets n CUs' worth of workgroups on every
+                                 XCD, the L1 kernel the rest; n < CUs per XCD (32) */
 } mega_moe_config;
 
 typedef struct mega_moe_handle mega_moe_handle;

@@ -82,7 +82,7 @@ def test_plan_overrides():
                                 dict(block_m=32, block_n=256),
                                 dict(hidden=7296, block_n=256), dict(activation_clamp=0.0),
                                 dict(activation_clamp=-1.0), dict(activation_clamp=math.nan),
-                                dict(fast_math=2)])
+                                dict(fast_math=2), dict(split_l2_cus=-1), dict(split_l2_cus=32)])
 def test_invalid_configs_are_rejected(kw):
     assert B.mega_moe_workspace_bytes(_cfg(**kw)) == -1
     with pytest.raises(B.MegaMoEError) as ei:

@@ -7,6 +7,7 @@ Shapes span several tiles and ragged tails: pool blocks only partly filled,
 experts with several pool blocks, a single expert, top-1, inactive slots.
 """
 
+import dataclasses
 import math
 
 import numpy as np
@@ -255,3 +256,35 @@ def test_too_many_tokens_is_rejected():
         assert ei.value.code == G.B.MEGA_MOE_ERR_INVALID_ARG
     finally:
         run.close()
+
+
+@pytest.mark.parametrize("name", ["ragged", "many_blocks", "skewed"])
+@pytest.mark.parametrize("l2_cus", [4, 12])
+def test_split_phases_match_fused(name, l2_cus):
+    # L1 and L2 tiles as two concurrent kernels on disjoint CU sets (the
+    # green-context split) compute every tile exactly as the fused kernel:
+    # identical bits, for FP8 and MXFP4 weights
+    for mx in (False, True):
+        wl = SMALL[name]
+        if mx:
+            wl = dataclasses.replace(wl, name=name + "_mxfp4", weight_format="mxfp4")
+        inp = S.make_inputs(wl)
+        outs = []
+        for split in (0, l2_cus):
+            print(f"[{name} mx={mx}] split_l2_cus {split}", flush=True)
+            run = G.Runner(inp, split_l2_cus=split)
+            try:
+                assert run.forward() == 0
+                v = run.views(inp["x"].shape[0])
+                outs.append((run.y().copy(), v["l2_acts"].copy(), v["comb"].copy()))
+            finally:
+                run.close()
+        for a, b in zip(*outs):
+            assert np.array_equal(a, b), (name, mx, l2_cus)
+
+
+def test_split_phases_reject_too_many_l2_cus():
+    inp, _ = _case("tiny")
+    with pytest.raises(B.MegaMoEError) as ei:
+        G.Runner(inp, split_l2_cus=40)
+    assert ei.value.code == B.MEGA_MOE_ERR_INVALID_ARG
