@@ -99,6 +99,11 @@ int check_config(const mega_moe_config* c) {
     if (c->split_l2_cus < 0 || c->split_l2_cus > 31)
         return fail(MEGA_MOE_ERR_INVALID_ARG, "split_l2_cus must be in [0, 31], got %d",
                     c->split_l2_cus);
+    if (c->keep_pool != 0 && c->keep_pool != 1)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "keep_pool must be 0 or 1");
+    // the expert kernel addresses rows of x with 32-bit byte offsets
+    if ((int64_t)c->max_tokens * c->hidden > ((int64_t)1 << 31) - 2 * (int64_t)c->hidden)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "max_tokens * hidden must stay below 2^31");
     return MEGA_MOE_OK;
 }
 
@@ -404,7 +409,7 @@ static int forward_impl(mega_moe_handle* h, int32_t T, const uint8_t* x, const f
     a.w2_sf = w.w2_sf;
     a.w2_e8 = w.w2_e8;
     a.y = y;
-    const int gather_blocks = a.R < 16384 ? a.R : 16384;
+    const int gather_blocks = h->cfg.keep_pool ? (a.R < 16384 ? a.R : 16384) : 0;
     const int call = h->prof_used < h->prof_max ? h->prof_used++ : -1;
     if (call >= 0) hipEventRecord(prof_event(h, call, 0), stream);
     launch_dispatch(a, gather_blocks, stream);

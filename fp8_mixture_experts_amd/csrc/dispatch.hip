@@ -334,7 +334,9 @@ void launch_dispatch(const MoeArgs& a, int gather_blocks, hipStream_t stream) {
         hipLaunchKernelGGL(moe_dispatch_scan, dim3(1), dim3(SCAN_THREADS), 0, stream, a);
         hipLaunchKernelGGL(moe_dispatch_scatter, dim3(a.num_chunks), dim3(DISPATCH_THREADS), 0, stream, a);
     }
-    hipLaunchKernelGGL(moe_dispatch_gather, dim3(gather_blocks), dim3(256), 0, stream, a);
+    // the pool copies are only for inspection (the expert kernel reads x)
+    if (gather_blocks > 0)
+        hipLaunchKernelGGL(moe_dispatch_gather, dim3(gather_blocks), dim3(256), 0, stream, a);
 }
 
 }  // namespace mega_moe

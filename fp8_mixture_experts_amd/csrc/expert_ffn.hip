@@ -354,7 +354,7 @@ struct Cfg {
     static constexpr int WAIT = (S - 2) * LPS;            // loads younger than the current step
     static constexpr int OFF_TILE = S * STAGE;            // per-tile area after the stages
     static constexpr int HS = BN / 2 + 4;                 // L1 epilogue h row stride (floats)
-    static constexpr int LDS_BYTES = OFF_TILE + MAX_W_SF * NSB * 4 + BM * 4 + 16;
+    static constexpr int LDS_BYTES = OFF_TILE + MAX_W_SF * NSB * 4 + BM * 4 + 16 + BM * 4;
     static_assert((A_BLK + B_BLK) % NW == 0 && A_BLK % NW == 0, "row blocks per wave");
     static_assert(!MX || BN == 128, "MXFP4 weights use 128-column tiles");
     static_assert(WAIT < 64, "vmcnt range");
@@ -370,6 +370,7 @@ struct Lds {
     // weight scales of the tile (FP8 weights): [NSB][KB]
     __device__ float* w_sf() const { return reinterpret_cast<float*>(base + C::OFF_TILE); }
     __device__ float* row_w() const { return w_sf() + MAX_W_SF * C::NSB; }   // top-k weight per row (L1)
+    // [0] the dequeued tile, [2..3] scratch, [4, 4 + BM) the L1 tile's x rows
     __device__ int* tile() const { return reinterpret_cast<int*>(row_w() + C::BM); }
 };
 
@@ -399,10 +400,16 @@ struct Loader {
     int sf_step;     // bytes between the scale groups of consecutive steps
 
     // ra: activation rows (row_a bytes each), rb: weight rows (row_b bytes),
-    // rs: activation scales (pool-minor, row stride P), rw: UE8M0 scale rows
-    // of the weight rows (row_w bytes; MXFP4 only)
+    // rs: activation scales, rw: UE8M0 scale rows of the weight rows (row_w
+    // bytes; MXFP4 only).  L1 tiles (HALVES 1) gather: arow[n] is the row of
+    // x (and of x_sf) that tile row n reads, or a row past the end of ra / rs
+    // for the padding rows, which then load as zeros; the scales are then
+    // one float per row (row stride row_s bytes, step kb at byte 4 kb).  L2
+    // tiles read the pool in order (arow unused) and its pool-minor scales
+    // (row stride P).
     __device__ Loader(__amdgpu_buffer_rsrc_t ra_, __amdgpu_buffer_rsrc_t rb_, int row_a, int row_b,
-                      __amdgpu_buffer_rsrc_t rs_, int P, __amdgpu_buffer_rsrc_t rw_, int row_w)
+                      __amdgpu_buffer_rsrc_t rs_, int P, __amdgpu_buffer_rsrc_t rw_, int row_w,
+                      const int* arow = nullptr, int row_s = 0)
         : ra(ra_), rb(rb_), rs(rs_), rw(rw_) {
         const int lane = threadIdx.x & 63;
         w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -411,7 +418,9 @@ struct Loader {
             const int b = C::NW * j + w;
             if (j < C::A_J) {
                 const int n = 8 * b + (lane >> 3);                  // activation row
-                voff[j] = n * row_a + 16 * ((lane & 7) ^ row_swz(n));
+                int src_row = n;
+                if constexpr (HALVES == 1) src_row = arow[n];
+                voff[j] = src_row * row_a + 16 * ((lane & 7) ^ row_swz(n));
             } else if constexpr (C::MX) {
                 const int n = 16 * (b - C::A_BLK) + (lane >> 2);    // MXFP4 weight row
                 voff[j] = n * row_b + 16 * ((lane & 3) ^ swz4(n));
@@ -420,11 +429,18 @@ struct Loader {
                 voff[j] = n * row_b + 16 * ((lane & 7) ^ row_swz(n));
             }
         }
-        // scale bytes [w*Q, w*Q + Q) of the step's 2*BM*4-byte scale area
-        const int off = w * Q + 16 * lane;
-        const int half = off / (C::BM * 4);
-        sf_voff = half * P * 4 + (off - half * C::BM * 4);
-        sf_step = HALVES * P * 4;
+        if constexpr (HALVES == 1) {
+            // one scale per lane: rows [w*BM/NW, (w+1)*BM/NW) of the tile
+            const int n = w * (C::BM / C::NW) + (lane & (C::BM / C::NW - 1));
+            sf_voff = arow[n] * row_s;
+            sf_step = 4;
+        } else {
+            // scale bytes [w*Q, w*Q + Q) of the step's 2*BM*4-byte scale area
+            const int off = w * Q + 16 * lane;
+            const int half = off / (C::BM * 4);
+            sf_voff = half * P * 4 + (off - half * C::BM * 4);
+            sf_step = HALVES * P * 4;
+        }
         wsc_voff = (32 * w + (lane & 31)) * row_w;
     }
 
@@ -439,8 +455,13 @@ struct Loader {
                 else dma16(rb, stage + (C::NW * j + w) * 1024, voff[j], soff_b);
             }
         }
-        if (lane < Q / 16 && (real || lane == 0))
-            dma16<AUX_ACT>(rs, stage + C::OFF_SF + w * Q, sf_voff, real ? kb * sf_step : 0);
+        if constexpr (HALVES == 1) {
+            if (lane < C::BM / C::NW && (real || lane == 0))
+                dma4(rs, stage + C::OFF_SF + 4 * w * (C::BM / C::NW), sf_voff, real ? kb * sf_step : 0);
+        } else {
+            if (lane < Q / 16 && (real || lane == 0))
+                dma16<AUX_ACT>(rs, stage + C::OFF_SF + w * Q, sf_voff, real ? kb * sf_step : 0);
+        }
         if constexpr (C::MX) {
             if (lane < 32 && (real || lane == 0))
                 dma4(rw, stage + C::OFF_WSC + 128 * w, wsc_voff, real ? kb * 4 : 0);
@@ -533,15 +554,23 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
         const float* wsf = a.w1_sf + ((size_t)e * a.nb1 + nb) * C::NSB * KB;
         for (int i = threadIdx.x; i < C::NSB * KB; i += NT) lds.w_sf()[i] = wsf[i];
     }
-    for (int r = threadIdx.x; r < BM; r += NT) lds.row_w()[r] = a.l1_w[row0 + r];
+    // the tile's rows come straight from x: tile row r < valid is route
+    // src[row0 + r] = t*k + j, which reads row t of x and x_sf and takes the
+    // top-k weight topk_w[t*k + j]; padding rows point one row past the end
+    // of x, where the buffer loads return zeros
+    for (int r = threadIdx.x; r < BM; r += NT) {
+        const int f = r < valid ? a.src[row0 + r] : -1;
+        lds.row_w()[r] = f >= 0 ? a.topk_w[f] : 0.0f;
+        lds.tile()[4 + r] = f >= 0 ? f / a.k : a.T;
+    }
     __syncthreads();
     const int row_b = C::MX ? H / 2 : H;
     const Loader<MS, BNT, 1, WF> ld(
-        make_rsrc(a.l1_acts + (size_t)row0 * H, (uint32_t)valid * H),
+        make_rsrc(a.x, (uint32_t)((size_t)a.T * H)),
         make_rsrc(a.w1 + wrow0 * row_b, (uint32_t)(BN * row_b)), H, row_b,
-        make_rsrc(a.l1_sf + row0, (uint32_t)(((KB - 1) * P + BM) * 4)), (int)P,
+        make_rsrc(a.x_sf, (uint32_t)((size_t)a.T * KB * 4)), (int)P,
         make_rsrc(C::MX ? a.w1_e8 + wrow0 * (H / 32) : nullptr, C::MX ? (uint32_t)(BN * (H / 32)) : 0u),
-        H / 32);
+        H / 32, lds.tile() + 4, KB * 4);
     // MXFP4: smallest and largest block scale this lane converted (reported
     // when outside 2^-23 .. 2^13, where the F16 conversion stops being exact)
     float sc_lo = 1.0f, sc_hi = 1.0f;

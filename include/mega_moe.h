@@ -81,6 +81,11 @@ typedef struct mega_moe_config {
                                  split of the PR357 review, sections 1 and 5.2): the
                                  L2 kernel gets n CUs' worth of workgroups on every
                                  XCD, the L1 kernel the rest; n < CUs per XCD (32) */
+    int32_t keep_pool;        /* 0 (default): the L1 tiles read each route's row of x,
+                                 its scales and top-k weight in place.  1: the dispatch
+                                 also copies them into the expert pool (the pages'
+                                 pull into the pool, SM90 design 9.2) so that the
+                                 l1_* views show them; results are the same */
 } mega_moe_config;
 
 typedef struct mega_moe_handle mega_moe_handle;
@@ -193,9 +198,10 @@ typedef struct mega_moe_views {
     int32_t* offsets;       /* [E+1]   pool segment starts, 128-aligned          */
     int32_t* slot_map;      /* [T*k]   pool row of route t*k+j, -1 if inactive   */
     int32_t* src;           /* [P]     route t*k+j held by a pool row, -1 = pad  */
-    uint8_t* l1_acts;       /* [P, H]  pool of FP8 rows                          */
-    float* l1_acts_sf;      /* [H/128, P] their scales (pool-row minor)          */
-    float* l1_topk_weights; /* [P]     their top-k weights                       */
+    uint8_t* l1_acts;       /* [P, H]  pool of FP8 rows (written only when the
+                               config sets keep_pool)                            */
+    float* l1_acts_sf;      /* [H/128, P] their scales (pool-row minor; keep_pool) */
+    float* l1_topk_weights; /* [P]     their top-k weights (keep_pool)           */
     uint8_t* l2_acts;       /* [P, I]  re-quantised SwiGLU output                */
     float* l2_acts_sf;      /* [I/64, P] its per-64 scales (pool-row minor)      */
     uint16_t* combine_buf;  /* [T*k, H] BF16 L2 partial of each active route     */

@@ -78,6 +78,7 @@ class Runner:
         T = inp["x"].shape[0]
         self.E, self.H, self.I, self.k = E, H, I, k
         self.mx = is_mxfp4(inp)
+        self.keep_pool = bool(cfg.get("keep_pool", 0))
         self.layer = B.MegaMoE(E, H, I, k, max_tokens if max_tokens is not None else T, **cfg)
         self.dev = to_device(inp)
 
@@ -109,12 +110,14 @@ class Runner:
         P = int(out["offsets"][-1])
         out["P"] = P
         out["src"] = d2h(v.src, (P,), np.int32)
-        out["l1_w"] = d2h(v.l1_topk_weights, (P,), np.float32)
-        out["l1_sf"] = d2h(v.l1_acts_sf, (H // 128, Pc), np.float32)[:, :P]
+        if self.keep_pool:      # the pool copies exist only when asked for
+            out["l1_w"] = d2h(v.l1_topk_weights, (P,), np.float32)
+            out["l1_sf"] = d2h(v.l1_acts_sf, (H // 128, Pc), np.float32)[:, :P]
         out["l2_sf"] = d2h(v.l2_acts_sf, (I // 64, Pc), np.float32)[:, :P]
         out["l2_acts"] = d2h(v.l2_acts, (P, I), np.uint8)
         if full:
-            out["l1_acts"] = d2h(v.l1_acts, (P, H), np.uint8)
+            if self.keep_pool:
+                out["l1_acts"] = d2h(v.l1_acts, (P, H), np.uint8)
             out["comb"] = d2h(v.combine_buf, (T * k, H), np.uint16)
         return out
 

@@ -50,9 +50,10 @@ def _compare_all(inp, ref, run, label):
     assert np.array_equal(v["slot_map"], ref["slot_map"]), label
     assert np.array_equal(v["src"], ref["src"]), label
     valid = ref["src"] >= 0
-    assert np.array_equal(v["l1_acts"][valid], ref["l1_acts"][valid]), label
-    assert np.array_equal(v["l1_sf"][:, valid], ref["l1_acts_sf"][:, valid]), label
-    assert np.array_equal(v["l1_w"][valid], ref["l1_w"][valid]), label
+    if run.keep_pool:
+        assert np.array_equal(v["l1_acts"][valid], ref["l1_acts"][valid]), label
+        assert np.array_equal(v["l1_sf"][:, valid], ref["l1_acts_sf"][:, valid]), label
+        assert np.array_equal(v["l1_w"][valid], ref["l1_w"][valid]), label
     G.check_codes(v["l2_acts"][valid], ref["l2_acts"][valid], label)
     G.check_sf(v["l2_sf"][:, valid], ref["l2_acts_sf"][:, valid], label)
     act = ref["active"].reshape(-1)
@@ -61,13 +62,16 @@ def _compare_all(inp, ref, run, label):
 
 
 @pytest.mark.parametrize("name", list(SMALL))
-def test_layer_matches_oracle(name):
+@pytest.mark.parametrize("keep_pool", [0, 1])
+def test_layer_matches_oracle(name, keep_pool):
+    # keep_pool 1 also materialises the pool copies, which must equal the
+    # oracle's bit for bit; the results must not depend on it
     inp, ref = _case(name)
-    run = G.Runner(inp)
+    run = G.Runner(inp, keep_pool=keep_pool)
     try:
         assert run.forward() == 0
-        err = _compare_all(inp, ref, run, name)
-        print(f"{name}: y rel frobenius {err:.2e}")
+        err = _compare_all(inp, ref, run, f"{name} keep_pool {keep_pool}")
+        print(f"{name} keep_pool {keep_pool}: y rel frobenius {err:.2e}")
     finally:
         run.close()
 

@@ -27,7 +27,7 @@ def test_full_size_workload(name):
     k = inp["topk_idx"].shape[1]
     E = inp["w1"].shape[0]
     print(f"[{name}] T={T} H={H} E={E} k={k}", flush=True)
-    run = G.Runner(inp)
+    run = G.Runner(inp, keep_pool=1)
     try:
         assert run.forward() == 0
         v = run.views(T, full=False)
