@@ -202,12 +202,14 @@ __device__ __forceinline__ v8h f16_of_pair(const v4i& raw, int h) {
 
 // MXFP4 weight rows in a stage: 64 bytes (128 E2M1 codes) per row.  The
 // 8 bytes that pair m (16-K parts 2m, 2m + 1) of lane half g needs: codes
-// K = 32m + 16g + [0, 16), the same K the FP8 activation parts carry.
-__device__ __forceinline__ uint2 fp4_pair_raw(const uint8_t* region, int s, int m) {
+// K = 32m + 16g + [0, 16), the same K the FP8 activation parts carry.  Read
+// as an integer vector, like every read of a stage (see stage_rows).
+typedef int v2i __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v2i fp4_pair_raw(const uint8_t* region, int s, int m) {
     const int L = threadIdx.x & 63;
     const int r = L & 31, g = L >> 5;
     const uint8_t* row = region + (32 * s + r) * 64;
-    return *reinterpret_cast<const uint2*>(row + 16 * (m ^ swz4(r)) + 8 * g);
+    return *reinterpret_cast<const v2i*>(row + 16 * (m ^ swz4(r)) + 8 * g);
 }
 
 // 16 bytes (32 codes, K = 64hh + 32g + [0, 32)) of 64-K half hh for the
@@ -606,7 +608,7 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                 for (int q = 0; q < LY::NG; ++q) wsc[q] = lane_wsc(stg + C::OFF_WSC, ly.g0 + q);
                 v16f d[LY::NJ][LY::NG];
                 if constexpr (LY::GRID) {
-                    uint2 rb[2][LY::NG];
+                    v2i rb[2][LY::NG];
                     v4i ra[2][LY::NJ];
                     auto read_pair = [&](int buf, int m) {
 #pragma unroll
@@ -631,7 +633,7 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                             v8h b16[LY::NG];
 #pragma unroll
                             for (int q = 0; q < LY::NG; ++q)
-                                b16[q] = f16_of_fp4(h ? rb[m & 1][q].y : rb[m & 1][q].x, sc[q]);
+                                b16[q] = f16_of_fp4((uint32_t)rb[m & 1][q][h], sc[q]);
 #pragma unroll
                             for (int j = 0; j < LY::NJ; ++j) {
                                 const v8h a16 = f16_of_pair(ra[m & 1][j], h);
@@ -645,12 +647,12 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                     v8h b16[8];
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        const uint2 raw = fp4_pair_raw(stg + C::OFF_B, ly.g0, m);
+                        const v2i raw = fp4_pair_raw(stg + C::OFF_B, ly.g0, m);
                         const float sc = e8_scale(wsc[0], m);
                         sc_lo = fminf(sc_lo, sc);
                         sc_hi = fmaxf(sc_hi, sc);
-                        b16[2 * m] = f16_of_fp4(raw.x, sc);
-                        b16[2 * m + 1] = f16_of_fp4(raw.y, sc);
+                        b16[2 * m] = f16_of_fp4((uint32_t)raw[0], sc);
+                        b16[2 * m + 1] = f16_of_fp4((uint32_t)raw[1], sc);
                     }
 #pragma unroll
                     for (int j = 0; j < LY::NJ; ++j) {
