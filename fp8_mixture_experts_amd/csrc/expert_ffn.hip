@@ -200,6 +200,32 @@ __device__ __forceinline__ v8h f16_of_pair(const v4i& raw, int h) {
     return v8h{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
 }
 
+// One column group times NJ slices (0 .. NJ-1) of a stage: the group's B
+// operand is already converted (b16, one v8h per 16-K part); the slices' MFMA
+// chains run interleaved part by part, so consecutive MFMAs are independent,
+// and each slice's raw A pair m + 1 is read while pair m is converted.
+template <int NJ>
+__device__ __forceinline__ void slice_chains(const uint8_t* stg, const v8h (&b16)[8], v16f (&d)[NJ]) {
+    const v16f zero = v16f{};
+    v4i ra[2][NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) ra[0][j] = frag_pair_raw(stg, j, 0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        if (m < 3) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) ra[(m + 1) & 1][j] = frag_pair_raw(stg, j, m + 1);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int p = 2 * m + h;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                d[j] = mfma_f16(b16[p], f16_of_pair(ra[m & 1][j], h), p == 0 ? zero : d[j]);
+        }
+    }
+}
+
 // MXFP4 weight rows in a stage: 64 bytes (128 E2M1 codes) per row.  The
 // 8 bytes that pair m (16-K parts 2m, 2m + 1) of lane half g needs: codes
 // K = 32m + 16g + [0, 16), the same K the FP8 activation parts carry.  Read
@@ -654,13 +680,10 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                         b16[2 * m] = f16_of_fp4((uint32_t)raw[0], sc);
                         b16[2 * m + 1] = f16_of_fp4((uint32_t)raw[1], sc);
                     }
+                    v16f dj[LY::NJ];
+                    slice_chains<LY::NJ>(stg, b16, dj);
 #pragma unroll
-                    for (int j = 0; j < LY::NJ; ++j) {
-                        const Frag fa = read_frag2(stg, j);
-                        d[j][0] = mfma_f16(b16[0], f16_part(fa.h[0], 0), zero);
-#pragma unroll
-                        for (int p = 1; p < 8; ++p) d[j][0] = mfma_f16(b16[p], f16_part(fa.h[p >> 2], p & 3), d[j][0]);
-                    }
+                    for (int j = 0; j < LY::NJ; ++j) d[j][0] = dj[j];
                 }
                 // no weight scale left to apply: promote by the row's x_sf
 #pragma unroll
@@ -715,19 +738,17 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                 }
             } else {
                 // one column group: its B operand converted once per step,
-                // then one MFMA chain per active slice
+                // then one MFMA chain per active slice, interleaved
                 const Frag fb = read_frag2(stg + C::OFF_B, ly.g0);
                 v8h b16[8];
 #pragma unroll
                 for (int p = 0; p < 8; ++p) b16[p] = f16_part(fb.h[p >> 2], p & 3);
+                v16f dj[LY::NJ];
+                slice_chains<LY::NJ>(stg, b16, dj);
 #pragma unroll
                 for (int j = 0; j < LY::NJ; ++j) {
-                    const Frag fa = read_frag2(stg, j);
                     const float svw = lane_row_scale(sfa, j) * sw;
-                    v16f d = mfma_f16(b16[0], f16_part(fa.h[0], 0), zero);
-#pragma unroll
-                    for (int p = 1; p < 8; ++p) d = mfma_f16(b16[p], f16_part(fa.h[p >> 2], p & 3), d);
-                    acc[j][0] = __builtin_elementwise_fma(d, v16f(svw), acc[j][0]);
+                    acc[j][0] = __builtin_elementwise_fma(dj[j], v16f(svw), acc[j][0]);
                 }
             }
         });
