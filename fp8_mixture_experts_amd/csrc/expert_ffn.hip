@@ -265,9 +265,12 @@ __device__ __forceinline__ float e8_scale(uint32_t w, int i) {
 }
 
 // The scale dword (four UE8M0 bytes, the step's 32-K blocks) of stored weight
-// row 32 s + lane % 32, read as an integer like the fragments.
+// row 32 s + lane % 32, read as an integer like the fragments: from the
+// step's stage (row_bytes 4) or from a four-step block (row_bytes 16, wsc_rows
+// already offset to the step's dword).
+template <int ROW_BYTES = 4>
 __device__ __forceinline__ uint32_t lane_wsc(const uint8_t* wsc_rows, int s) {
-    return (uint32_t)*reinterpret_cast<const int*>(wsc_rows + 4 * (32 * s + (threadIdx.x & 31)));
+    return (uint32_t)*reinterpret_cast<const int*>(wsc_rows + ROW_BYTES * (32 * s + (threadIdx.x & 31)));
 }
 
 // Accumulator layout of the 32x32 MFMA: register v of lane l holds row
@@ -358,7 +361,11 @@ struct Cfg {
     static constexpr int B_ROW = MX ? BK / 2 : BK;        // weight bytes per row per step
     static constexpr int A_BYTES = BM * BK;               // activation rows of a stage
     static constexpr int B_BYTES = BN * B_ROW;            // weight rows of a stage
-    static constexpr int WSC_BYTES = MX ? BN * 4 : 0;     // UE8M0 scales of the weight rows
+    // UE8M0 scales of the weight rows: in the stage (one dword per row and
+    // step), or, on tiles below 128 rows, in blocks of four steps (16 bytes
+    // per row, double buffered outside the stages)
+    static constexpr bool WSC_BLOCK = MX && MS <= 2;
+    static constexpr int WSC_BYTES = MX && !WSC_BLOCK ? BN * 4 : 0;
     static constexpr int SF_BYTES = 2 * BM * 4;           // per-row scales of a step (2 halves in L2)
     static constexpr int OFF_B = A_BYTES;
     static constexpr int OFF_WSC = OFF_B + B_BYTES;
@@ -380,7 +387,9 @@ struct Cfg {
     static constexpr int A_J = A_BLK / NW;                // of which activation rows
     static constexpr int LPS = PT + 1 + (MX ? 1 : 0);     // load instructions per wave per step
     static constexpr int WAIT = (S - 2) * LPS;            // loads younger than the current step
-    static constexpr int OFF_TILE = S * STAGE;            // per-tile area after the stages
+    static constexpr int OFF_WSB = S * STAGE;             // scale blocks [2][BN][16 bytes]
+    static constexpr int OFF_DUMMY = OFF_WSB + (WSC_BLOCK ? 2 * BN * 16 : 0);  // 16 bytes per wave
+    static constexpr int OFF_TILE = OFF_DUMMY + (WSC_BLOCK ? 64 * NW / 4 : 0);  // per-tile area
     static constexpr int HS = BN / 2 + 4;                 // L1 epilogue h row stride (floats)
     static constexpr int LDS_BYTES = OFF_TILE + MAX_W_SF * NSB * 4 + BM * 4 + 16 + BM * 4;
     static_assert((A_BLK + B_BLK) % NW == 0 && A_BLK % NW == 0, "row blocks per wave");
@@ -395,6 +404,8 @@ struct Lds {
     using C = Cfg<MS, BNT, WF>;
     uint8_t* base;
     __device__ uint8_t* stage(int i) const { return base + i * C::STAGE; }
+    __device__ uint8_t* wsb(int buf) const { return base + C::OFF_WSB + buf * C::BN * 16; }
+    __device__ uint8_t* dummy() const { return base + C::OFF_DUMMY; }
     // weight scales of the tile (FP8 weights): [NSB][KB]
     __device__ float* w_sf() const { return reinterpret_cast<float*>(base + C::OFF_TILE); }
     __device__ float* row_w() const { return w_sf() + MAX_W_SF * C::NSB; }   // top-k weight per row (L1)
@@ -472,7 +483,8 @@ struct Loader {
         wsc_voff = (32 * w + (lane & 31)) * row_w;
     }
 
-    __device__ __forceinline__ void issue(uint8_t* stage, int kb, bool real) const {
+    // lds_base: the workgroup's LDS (for the scale blocks and the dummy slot)
+    __device__ __forceinline__ void issue(uint8_t* stage, int kb, bool real, uint8_t* lds_base) const {
         const int lane = threadIdx.x & 63;
         const int soff_a = real ? kb * BK : 0;
         const int soff_b = real ? kb * C::B_ROW : 0;
@@ -490,7 +502,18 @@ struct Loader {
             if (lane < Q / 16 && (real || lane == 0))
                 dma16<AUX_ACT>(rs, stage + C::OFF_SF + w * Q, sf_voff, real ? kb * sf_step : 0);
         }
-        if constexpr (C::MX) {
+        if constexpr (C::WSC_BLOCK) {
+            // every fourth step: steps kb .. kb + 3 of the wave's 32 rows, 16
+            // bytes each, into buffer (kb / 4) % 2; other steps issue one
+            // lane into the wave's dummy slot so the count stays the same
+            if (real && (kb & 3) == 0) {
+                if (lane < 32)
+                    dma16(rw, lds_base + C::OFF_WSB + ((kb >> 2) & 1) * C::BN * 16 + 512 * w, wsc_voff,
+                          4 * kb);
+            } else if (lane == 0) {
+                dma16(rw, lds_base + C::OFF_DUMMY + 16 * w, 0, 0);
+            }
+        } else if constexpr (C::MX) {
             if (lane < 32 && (real || lane == 0))
                 dma4(rw, stage + C::OFF_WSC + 128 * w, wsc_voff, real ? kb * 4 : 0);
         }
@@ -510,12 +533,12 @@ __device__ __forceinline__ void k_loop(const Loader<MS, BNT, HALVES, WF>& ld, co
     using C = Cfg<MS, BNT, WF>;
     constexpr int S = C::S;
 #pragma unroll
-    for (int d = 0; d < S - 1; ++d) ld.issue(lds.stage(d), d, d < KB);
+    for (int d = 0; d < S - 1; ++d) ld.issue(lds.stage(d), d, d < KB, lds.base);
     int cur = 0;
     for (int kb = 0; kb < KB; ++kb) {
         wait_barrier<C::WAIT>();
         const int nk = kb + S - 1;
-        ld.issue(lds.stage(cur == 0 ? S - 1 : cur - 1), nk, nk < KB);
+        ld.issue(lds.stage(cur == 0 ? S - 1 : cur - 1), nk, nk < KB, lds.base);
         compute(lds.stage(cur), kb);
         cur = cur == S - 1 ? 0 : cur + 1;
     }
@@ -631,7 +654,12 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                 // in, then the same F16 MFMA chains as FP8 weights
                 uint32_t wsc[LY::NG];
 #pragma unroll
-                for (int q = 0; q < LY::NG; ++q) wsc[q] = lane_wsc(stg + C::OFF_WSC, ly.g0 + q);
+                for (int q = 0; q < LY::NG; ++q) {
+                    if constexpr (C::WSC_BLOCK)
+                        wsc[q] = lane_wsc<16>(lds.wsb((kb >> 2) & 1) + 4 * (kb & 3), ly.g0 + q);
+                    else
+                        wsc[q] = lane_wsc(stg + C::OFF_WSC, ly.g0 + q);
+                }
                 v16f d[LY::NJ][LY::NG];
                 if constexpr (LY::GRID) {
                     v2i rb[2][LY::NG];
@@ -897,7 +925,10 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                 v4i fb[LY::NG][2];
 #pragma unroll
                 for (int q = 0; q < LY::NG; ++q) {
-                    wsc[q] = lane_wsc(stg + C::OFF_WSC, ly.g0 + q);
+                    if constexpr (C::WSC_BLOCK)
+                        wsc[q] = lane_wsc<16>(lds.wsb((kb >> 2) & 1) + 4 * (kb & 3), ly.g0 + q);
+                    else
+                        wsc[q] = lane_wsc(stg + C::OFF_WSC, ly.g0 + q);
                     fb[q][0] = fp4_half_raw(stg + C::OFF_B, ly.g0 + q, 0);
                     fb[q][1] = fp4_half_raw(stg + C::OFF_B, ly.g0 + q, 1);
                 }
