@@ -79,7 +79,6 @@ namespace mega_moe {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
@@ -229,7 +228,7 @@ __device__ __forceinline__ void slice_chains(const uint8_t* stg, const v8h (&b16
 // MXFP4 weight rows in a stage: 64 bytes (128 E2M1 codes) per row.  The
 // 8 bytes that pair m (16-K parts 2m, 2m + 1) of lane half g needs: codes
 // K = 32m + 16g + [0, 16), the same K the FP8 activation parts carry.  Read
-// as an integer vector, like every read of a stage (see stage_rows).
+// as an integer vector, like every read of a stage (see lane_row_scale).
 typedef int v2i __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ v2i fp4_pair_raw(const uint8_t* region, int s, int m) {
     const int L = threadIdx.x & 63;
@@ -273,48 +272,18 @@ __device__ __forceinline__ uint32_t lane_wsc(const uint8_t* wsc_rows, int s) {
     return (uint32_t)*reinterpret_cast<const int*>(wsc_rows + ROW_BYTES * (32 * s + (threadIdx.x & 31)));
 }
 
-// Accumulator layout of the 32x32 MFMA: register v of lane l holds row
-// 8*(v/4) + 4*(l/32) + v%4 and column l%32.  A lane's 16 rows come in four
-// runs of four consecutive rows, so per-row vectors load as four float4.
-__device__ __forceinline__ int acc_row(int v) {
-    return 8 * (v >> 2) + 4 * ((threadIdx.x >> 5) & 1) + (v & 3);
-}
-
-// Per-row vector in accumulator layout (four float4 runs) as one v16f.
-__device__ __forceinline__ v16f row_vec(const float* base) {
-    const int g4 = 4 * ((threadIdx.x >> 5) & 1);
-    const float4 a = *reinterpret_cast<const float4*>(base + g4);
-    const float4 b = *reinterpret_cast<const float4*>(base + 8 + g4);
-    const float4 c = *reinterpret_cast<const float4*>(base + 16 + g4);
-    const float4 d = *reinterpret_cast<const float4*>(base + 24 + g4);
-    return v16f{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
-}
-
 // The scale of this lane's row of a 32-row slice (result blocks are
-// transposed: a lane holds one activation row), read as an
-// integer and reinterpreted for the same reason as stage_rows below.
+// transposed: a lane holds one activation row).  Every read of a stage is an
+// integer read, reinterpreted where needed: the compiler treats a float- or
+// struct-typed LDS read of a stage as possibly aliasing the direct loads
+// still in flight into the other stages and would drain all of them
+// (vmcnt(0)) before it, while the k loop's wait and barrier already order
+// these reads.  (Issuing them as inline assembly instead is unsafe: the
+// compiler then cannot insert the wait states between an MFMA still reading
+// a register and the LDS read that overwrites it.)
 __device__ __forceinline__ float lane_row_scale(const uint8_t* sf_rows, int slice) {
     const int r = 32 * slice + (threadIdx.x & 31);
     return __builtin_bit_cast(float, *reinterpret_cast<const int*>(sf_rows + 4 * r));
-}
-
-// The per-row scales of a step, read from its stage in accumulator layout.
-// They are read as 16-byte integer vectors, like the operand fragments, and
-// reinterpreted: the compiler treats a float-typed LDS read of the stage as
-// possibly aliasing the direct loads still in flight into the other stages
-// and would drain all of them (vmcnt(0)) before it, while the k loop's wait
-// and barrier already order these reads.  (Issuing them as inline assembly
-// instead is unsafe: the compiler then cannot insert the wait states between
-// an MFMA still reading a register and the LDS read that overwrites it.)
-__device__ __forceinline__ v16f stage_rows(const uint8_t* base) {
-    const int g = 16 * ((threadIdx.x >> 5) & 1);
-    const v4i a = *reinterpret_cast<const v4i*>(base + g);
-    const v4i b = *reinterpret_cast<const v4i*>(base + 32 + g);
-    const v4i c = *reinterpret_cast<const v4i*>(base + 64 + g);
-    const v4i d = *reinterpret_cast<const v4i*>(base + 96 + g);
-    const v16i u = v16i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3],
-                        c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
-    return __builtin_bit_cast(v16f, u);
 }
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
@@ -341,7 +310,7 @@ __device__ __forceinline__ float silu_up(float g, float u, float clamp) {
     }
 }
 
-// The value of another lane by a DPP move (CTRL: quad_perm or row_ror).
+// The value of another lane by a DPP move (CTRL: a quad_perm pattern).
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
