@@ -20,7 +20,7 @@ from fp8_mixture_experts_amd import binding as B
 from fp8_mixture_experts_amd import synthetic as S
 from oracle import moe
 from tests import gpu_util as G
-from tests.test_gpu_layer import SMALL, _compare_all
+from tests.test_gpu_layer import EDGE, SMALL, _compare_all
 
 pytestmark = pytest.mark.gpu
 
@@ -115,3 +115,22 @@ def test_mxfp4_and_fp8_calls_share_a_handle():
             G.check_y(run.y(dev8), fp8_ref["y"], "skewed fp8")
     finally:
         run.close()
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_mxfp4_edge_shapes_match_oracle(name):
+    # the largest hidden / intermediate (64 scale blocks of a weight row
+    # block), top-k equal to the expert count, one expert with many pool
+    # blocks and a single token, with MXFP4 weights, at the planned, 64- and
+    # 128-row tiles
+    wl = dataclasses.replace(EDGE[name], name=name + "_mxfp4", weight_format="mxfp4")
+    inp = S.make_inputs(wl)
+    ref = moe.forward(inp)
+    for bm in (0, 64, 128):
+        print(f"[{name} mxfp4] block_m {bm}", flush=True)
+        run = G.Runner(inp, block_m=bm)
+        try:
+            assert run.forward() == 0
+            _compare_all(inp, ref, run, f"{name} mxfp4 block_m {bm}")
+        finally:
+            run.close()
