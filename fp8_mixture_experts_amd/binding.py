@@ -29,7 +29,7 @@ MEGA_MOE_DEVERR_SCALE_RANGE = 0x4
 EXPORTS = ["mega_moe_create", "mega_moe_forward", "mega_moe_forward_mxfp4", "mega_moe_destroy",
            "mega_moe_get_status",
            "mega_moe_last_error", "mega_moe_workspace_bytes", "mega_moe_token_alignment",
-           "mega_moe_plan", "mega_moe_get_views", "mega_moe_set_recv_stats",
+           "mega_moe_plan", "mega_moe_tile_order", "mega_moe_get_views", "mega_moe_set_recv_stats",
            "mega_moe_transform_w1", "mega_moe_profile_begin",
            "mega_moe_profile_end"]
 
@@ -90,6 +90,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mega_moe_plan.argtypes = [ctypes.POINTER(mega_moe_config), i32,
                                   ctypes.POINTER(mega_moe_plan_info)]
     lib.mega_moe_plan.restype = ctypes.c_int
+    lib.mega_moe_tile_order.argtypes = [ctypes.POINTER(mega_moe_plan_info), i32, i32, i32,
+                                        ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.mega_moe_tile_order.restype = ctypes.c_int
     lib.mega_moe_get_views.argtypes = [vp, ctypes.POINTER(mega_moe_views)]
     lib.mega_moe_get_views.restype = ctypes.c_int
     lib.mega_moe_transform_w1.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
@@ -175,6 +178,17 @@ def mega_moe_plan(cfg: mega_moe_config, num_tokens: int) -> mega_moe_plan_info:
     out = mega_moe_plan_info()
     _check(load().mega_moe_plan(ctypes.byref(cfg), num_tokens, ctypes.byref(out)))
     return out
+
+
+def mega_moe_tile_order(plan: mega_moe_plan_info, total_mb: int, n_xcd: int, phase: int):
+    """The expert kernel's tile order: (pool block, N block) lists over all
+    XCD ranges, each XCD's tiles in queue order (phase 1 L1, phase 2 L2)."""
+    nbs = plan.l1_n_blocks if phase == 1 else plan.l2_n_blocks
+    n = max(total_mb * nbs, 0)
+    pb = (ctypes.c_int32 * max(n, 1))()
+    nb = (ctypes.c_int32 * max(n, 1))()
+    _check(load().mega_moe_tile_order(ctypes.byref(plan), total_mb, n_xcd, phase, pb, nb))
+    return list(pb[:n]), list(nb[:n])
 
 
 def mega_moe_get_views(handle) -> mega_moe_views:

@@ -12,6 +12,7 @@
 
 #include "mega_moe.h"
 #include "moe_args.h"
+#include "schedule.h"
 
 namespace mega_moe {
 void launch_dispatch(const MoeArgs& a, int gather_blocks, hipStream_t stream);
@@ -258,6 +259,34 @@ int mega_moe_plan(const mega_moe_config* cfg, int32_t num_tokens, mega_moe_plan_
     return ok();
 }
 
+int mega_moe_tile_order(const mega_moe_plan_info* plan, int32_t total_mb, int32_t n_xcd,
+                        int32_t phase, int32_t* pb_out, int32_t* nb_out) {
+    if (!plan) return fail(MEGA_MOE_ERR_INVALID_ARG, "plan is NULL");
+    if (plan->block_m != 32 && plan->block_m != 64 && plan->block_m != 128)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "plan block_m %d is not 32, 64 or 128", plan->block_m);
+    if (total_mb < 0) return fail(MEGA_MOE_ERR_INVALID_ARG, "total_mb < 0");
+    if (n_xcd < 1 || n_xcd > MAX_XCD)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "n_xcd must be in [1, %d]", MAX_XCD);
+    if (phase != 1 && phase != 2) return fail(MEGA_MOE_ERR_INVALID_ARG, "phase must be 1 or 2");
+    const int nbs = phase == 1 ? plan->l1_n_blocks : plan->l2_n_blocks;
+    if (nbs < 1) return fail(MEGA_MOE_ERR_INVALID_ARG, "plan has no N blocks for phase %d", phase);
+    if (total_mb > 0 && (!pb_out || !nb_out))
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "an output array is NULL");
+    const int G = xcd_group_for(plan->block_m);
+    int64_t i = 0;
+    for (int x = 0; x < n_xcd; ++x) {
+        int lo, cnt;
+        xcd_range(total_mb, n_xcd, x, lo, cnt);
+        for (int u = 0; u < cnt * nbs; ++u, ++i) {
+            int j, nb;
+            tile_coords(u, cnt, nbs, G, plan->l2_n_major != 0, j, nb);
+            pb_out[i] = lo + j;
+            nb_out[i] = nb;
+        }
+    }
+    return ok();
+}
+
 int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out) {
     if (!out) return fail(MEGA_MOE_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
@@ -395,7 +424,7 @@ static int forward_impl(mega_moe_handle* h, int32_t T, const uint8_t* x, const f
     a.nb1 = p.l1_n_blocks;
     a.nb2 = p.l2_n_blocks;
     a.n_major = p.l2_n_major;
-    a.xcd_group = p.block_m == 32 ? 4 : (p.block_m == 64 ? 2 : 4);
+    a.xcd_group = xcd_group_for(p.block_m);
     a.num_chunks = (a.R + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK;
     a.x = x;
     a.x_sf = x_sf;

@@ -21,6 +21,7 @@
 #include <hip/hip_runtime.h>
 
 #include "moe_args.h"
+#include "schedule.h"
 #include "mega_moe.h"
 
 namespace mega_moe {
@@ -130,15 +131,13 @@ __device__ void finish_counts(const MoeArgs& a, const int* s_count, int* s_off, 
         if (r < pad) a.src[s_off[ex] + c + r] = -1;
     }
 
-    // Per-XCD work: XCD x takes the contiguous pool blocks [x*M/n, (x+1)*M/n)
-    // of the M pool blocks (expert-major), so every XCD gets the same number
-    // of blocks (+-1) and consecutive blocks of one expert mostly share an
-    // XCD and its L2.
+    // Per-XCD work: XCD x takes a contiguous range of the M pool blocks
+    // (expert-major)
     if (tid < a.n_xcd) {
-        const int lo = (int)((int64_t)total_mb * tid / a.n_xcd);
-        const int hi = (int)((int64_t)total_mb * (tid + 1) / a.n_xcd);
+        int lo, cnt;
+        xcd_range(total_mb, a.n_xcd, tid, lo, cnt);
         a.xcd_info[2 * tid] = lo;
-        a.xcd_info[2 * tid + 1] = hi - lo;
+        a.xcd_info[2 * tid + 1] = cnt;
     }
 
     // expert of every pool block, and a cleared arrival counter for it

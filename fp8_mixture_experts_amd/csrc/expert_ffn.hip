@@ -72,6 +72,7 @@
 #include <hip/hip_runtime.h>
 
 #include "moe_args.h"
+#include "schedule.h"
 #include "mega_moe.h"
 
 namespace mega_moe {
@@ -967,23 +968,6 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
             }
         }
     }
-}
-
-// Tile u of a range of `cnt` pool blocks x `nbs` N blocks.  Row-major keeps a
-// pool block's N blocks together; N-major runs each N block across the (at most
-// G) pool blocks of a group, so they share the weight block through L2.
-__device__ __forceinline__ void tile_coords(int u, int cnt, int nbs, int G, bool n_major, int& j,
-                                            int& nb) {
-    if (!n_major) {
-        j = u / nbs;
-        nb = u - j * nbs;
-        return;
-    }
-    const int k = u / (G * nbs);
-    const int within = u - k * G * nbs;
-    const int g = min(G, cnt - k * G);
-    nb = within / g;
-    j = k * G + (within - nb * g);
 }
 
 // Two workgroups of four waves per CU, one wave of each per SIMD; the launch

@@ -189,6 +189,23 @@ typedef struct mega_moe_plan_info {
 int mega_moe_plan(const mega_moe_config* cfg, int32_t num_tokens, mega_moe_plan_info* out);
 
 /*
+ * The expert kernel's tile order for a plan (a host-side query; needs no GPU).
+ * The M pool blocks of a call are split into n_xcd contiguous ranges, XCD x
+ * taking [x*M/n_xcd, (x+1)*M/n_xcd); that XCD's workgroups take the tiles of
+ * its range from its own queue, all L1 tiles (phase 1) before the L2 tiles
+ * (phase 2), each tile one pool block times one N block of plan->block_n
+ * columns (SM90 design 12.2: N-major when plan->l2_n_major, else row-major).
+ * Fills pb_out[i], nb_out[i] (host arrays of total_mb * N entries, N =
+ * plan->l1_n_blocks or plan->l2_n_blocks) with the absolute pool block and N
+ * block of the i-th tile: XCD 0's tiles in queue order, then XCD 1's, and so
+ * on.  Returns MEGA_MOE_ERR_INVALID_ARG for a NULL plan or output, a block_m
+ * other than 32/64/128, total_mb < 0, n_xcd outside [1, 16] or a phase other
+ * than 1 or 2.
+ */
+int mega_moe_tile_order(const mega_moe_plan_info* plan, int32_t total_mb, int32_t n_xcd,
+                        int32_t phase, int32_t* pb_out, int32_t* nb_out);
+
+/*
  * Device views of the intermediates of the last forward call (the buffer views
  * of SM90 design 16.1 / "PR357 review" 3.1), valid once its stream has
  * synchronised and until the next call.  P = pool_rows_capacity.
