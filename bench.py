@@ -226,6 +226,11 @@ def main():
         "pct_roofline": 100.0 * t_roof / s,
         "kernel_ms": {"dispatch": float(k_ms[:, 0].mean()), "expert": expert_ms,
                       "combine": float(k_ms[:, 2].mean())},
+        # per-step event times of the same kernels: median and minimum
+        "kernel_ms_median": {n: float(np.median(k_ms[:, i]))
+                             for i, n in enumerate(("dispatch", "expert", "combine"))},
+        "kernel_ms_min": {n: float(k_ms[:, i].min())
+                          for i, n in enumerate(("dispatch", "expert", "combine"))},
         "ms_per_step_with_events": (t3 - t2) * 1e3 / args.steps,
         "roofline": roof,
     }
