@@ -1,13 +1,14 @@
 // Dispatch of the expert layer: per-expert histogram, prefix scan into
-// 128-aligned pool segments, a stable slot for every route and the copy of
-// each routed token into its expert's pool ("MegaMoE SM90 Implementation
-// Design (Final)" 3.3 phase 1 and 9.2; one GPU, so every source is local).
+// 128-aligned pool segments, a stable slot for every route and, when the
+// layer keeps the pool, the copy of each routed token into its expert's pool
+// ("MegaMoE SM90 Implementation Design (Final)" 3.3 phase 1 and 9.2; one GPU,
+// so every source is local).  Without the pool copy the expert kernel's L1
+// tiles read each route's row of x in place through `src`.
 //
-// Up to 4096 routes: two launches on the caller's stream,
+// Up to 4096 routes: one launch on the caller's stream,
 //   moe_dispatch_small   one workgroup: histogram, scan, stable ranks, slot
 //                        map and source metadata, resets
-//   moe_dispatch_gather  (below);
-// larger batches: four,
+// larger batches: three,
 //   moe_dispatch_count   one workgroup per chunk of 1024 routes: histogram
 //   moe_dispatch_scan    one workgroup: per-expert scan over chunks, the
 //                        wavefront prefix scan over experts (offsets, pool
@@ -16,6 +17,7 @@
 //   moe_dispatch_scatter one workgroup per chunk: stable rank of every route
 //                        inside its expert (wave ballots), slot map and source
 //                        metadata
+// and, with the pool kept, one more:
 //   moe_dispatch_gather  copy of the FP8 row, its scales and its top-k weight
 //                        into the pool row of every route
 #include <hip/hip_runtime.h>

@@ -388,9 +388,11 @@ struct Lds {
 // block), then weight rows (8 FP8 rows of 128 bytes, or 16 MXFP4 rows of 64
 // bytes): lane q takes row q / (chunks per row) of its block and the chunk
 // whose swizzled position is q % (chunks per row).  Each wave then loads a
-// quarter of the step's per-row activation scales (one 64-row group of
-// l1_sf, or the two 64-K halves of l2_sf, in the pool-minor layout) and, with
-// MXFP4 weights, the UE8M0 dword (four 32-K blocks) of its 32 weight rows.
+// quarter of the step's per-row activation scales (L1 tiles: one float per
+// tile row, from that route's row of x_sf; L2 tiles: the two 64-K halves of
+// l2_sf, in the pool-minor layout) and, with MXFP4 weights, the UE8M0 scales
+// of its 32 weight rows: the step's dword (four 32-K blocks) of every row, or
+// on tiles below 128 rows 16 bytes per row (four steps) every fourth step.
 // A step past the end (real = false) still issues the same number of
 // instructions, from lane 0 only, so every wave's count of outstanding loads
 // is the same at every step.

@@ -28,7 +28,8 @@ struct MoeArgs {
     int32_t block_n;    // output columns per expert-kernel tile (128 or 256)
     int32_t nb1;        // L1 N blocks: 2I / block_n
     int32_t nb2;        // L2 N blocks: H / block_n
-    int32_t n_major;    // L2 tile order: 1 = consecutive tiles share a W2 N block
+    int32_t n_major;    // tile order of both phases: 1 = N-major (the pool blocks of a
+                        // group take each weight N block in turn), 0 = row-major
     int32_t num_chunks; // dispatch chunks of DISPATCH_CHUNK routes
     uint32_t wait_spin_limit;  // bound on one L2 tile's wait for its L1 tiles
     int32_t n_xcd;      // accelerator complex dies (each with its own L2) of the device
@@ -60,9 +61,9 @@ struct MoeArgs {
     int32_t* src;         // [P_cap]
     int32_t* chunk_hist;  // [num_chunks, E]
     int32_t* chunk_base;  // [num_chunks, E]
-    uint8_t* l1_acts;     // [P_cap, H]
-    float* l1_sf;         // [H/128, P_cap]
-    float* l1_w;          // [P_cap]
+    uint8_t* l1_acts;     // [P_cap, H]  pool copy of the routed rows (kept pool only)
+    float* l1_sf;         // [H/128, P_cap]  their scales (kept pool only)
+    float* l1_w;          // [P_cap]  their top-k weights (kept pool only)
     uint8_t* l2_acts;     // [P_cap, I]
     float* l2_sf;         // [I/64, P_cap]
     uint16_t* comb;       // [R, H]

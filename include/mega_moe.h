@@ -8,9 +8,11 @@
  * token is local.  One forward call computes, on the caller's HIP stream:
  *
  *   1. dispatch       per-expert counts, 128-aligned pool offsets, a stable
- *                     slot per (token, top-k slot) route, source metadata, and
- *                     the permuted per-expert pool of FP8 rows, their float
- *                     scales and top-k weights            (SM90 design 3.3, 9.2)
+ *                     slot per (token, top-k slot) route and source metadata;
+ *                     the L1 tiles then read each route's FP8 row, float
+ *                     scales and top-k weight in place (with keep_pool, the
+ *                     dispatch also copies them into the permuted per-expert
+ *                     pool)                               (SM90 design 3.3, 9.2)
  *   2. L1 GEMM        FP8 x FP8 with one float scale per 128 K for the
  *                     activations (per token) and per 128x128 block for W1;
  *                     W1 rows are gate/up interleaved by 8  (5.1-5.3, 15.1-15.2)
