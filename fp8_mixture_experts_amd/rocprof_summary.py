@@ -22,23 +22,39 @@ from __future__ import annotations
 import glob
 import hashlib
 import os
+import re
 import sqlite3
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 EXPERT_KERNEL = "moe_expert_ffn"
 COPY_KERNELS = ("copyBuffer", "copy_kernel", "CopyKernel")
 
 
+_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
+
+
+def code_text(src: str) -> str:
+    """C/C++/HIP source without its comments, whitespace runs collapsed."""
+    def keep(m):
+        t = m.group(0)
+        return " " if t.startswith("/") else t
+    return " ".join(_TOKENS.sub(keep, src).split())
+
+
 def sources_sha256() -> str:
-    """Hash of every library source: a counter reading is stale once it changes."""
+    """Hash of the code (comments and layout ignored) of every library source
+    and of the public header: a counter reading is stale once it changes."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".cpp", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    files = [os.path.join(CSRC, n) for n in sorted(os.listdir(CSRC))
+             if n.endswith((".hip", ".cpp", ".h"))]
+    files += [os.path.join(INCLUDE, n) for n in sorted(os.listdir(INCLUDE)) if n.endswith(".h")]
+    for path in files:
+        h.update(os.path.basename(path).encode())
+        with open(path, encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 
