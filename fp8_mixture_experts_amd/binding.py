@@ -90,8 +90,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mega_moe_plan.argtypes = [ctypes.POINTER(mega_moe_config), i32,
                                   ctypes.POINTER(mega_moe_plan_info)]
     lib.mega_moe_plan.restype = ctypes.c_int
-    lib.mega_moe_tile_order.argtypes = [ctypes.POINTER(mega_moe_plan_info), i32, i32, i32,
-                                        ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.mega_moe_tile_order.argtypes = [ctypes.POINTER(mega_moe_plan_info), i32, ctypes.POINTER(i32),
+                                        i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.mega_moe_tile_order.restype = ctypes.c_int
     lib.mega_moe_get_views.argtypes = [vp, ctypes.POINTER(mega_moe_views)]
     lib.mega_moe_get_views.restype = ctypes.c_int
@@ -180,14 +180,18 @@ def mega_moe_plan(cfg: mega_moe_config, num_tokens: int) -> mega_moe_plan_info:
     return out
 
 
-def mega_moe_tile_order(plan: mega_moe_plan_info, total_mb: int, n_xcd: int, phase: int):
-    """The expert kernel's tile order: (pool block, N block) lists over all
-    XCD ranges, each XCD's tiles in queue order (phase 1 L1, phase 2 L2)."""
+def mega_moe_tile_order(plan: mega_moe_plan_info, block_start, n_xcd: int, phase: int):
+    """The expert kernel's tile order for pool blocks laid out by block_start
+    (each expert's first pool block, then the total): (pool block, N block)
+    lists over all XCD ranges, each XCD's tiles in queue order (phase 1 L1,
+    phase 2 L2)."""
+    E = len(block_start) - 1
+    starts = (ctypes.c_int32 * (E + 1))(*block_start)
     nbs = plan.l1_n_blocks if phase == 1 else plan.l2_n_blocks
-    n = max(total_mb * nbs, 0)
+    n = max(block_start[-1] * nbs, 0) if E >= 0 else 0
     pb = (ctypes.c_int32 * max(n, 1))()
     nb = (ctypes.c_int32 * max(n, 1))()
-    _check(load().mega_moe_tile_order(ctypes.byref(plan), total_mb, n_xcd, phase, pb, nb))
+    _check(load().mega_moe_tile_order(ctypes.byref(plan), E, starts, n_xcd, phase, pb, nb))
     return list(pb[:n]), list(nb[:n])
 
 

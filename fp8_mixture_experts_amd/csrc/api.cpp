@@ -259,28 +259,39 @@ int mega_moe_plan(const mega_moe_config* cfg, int32_t num_tokens, mega_moe_plan_
     return ok();
 }
 
-int mega_moe_tile_order(const mega_moe_plan_info* plan, int32_t total_mb, int32_t n_xcd,
-                        int32_t phase, int32_t* pb_out, int32_t* nb_out) {
-    if (!plan) return fail(MEGA_MOE_ERR_INVALID_ARG, "plan is NULL");
+int mega_moe_tile_order(const mega_moe_plan_info* plan, int32_t num_experts,
+                        const int32_t* block_start, int32_t n_xcd, int32_t phase,
+                        int32_t* pb_out, int32_t* nb_out) {
+    if (!plan || !block_start) return fail(MEGA_MOE_ERR_INVALID_ARG, "plan or block_start is NULL");
     if (plan->block_m != 32 && plan->block_m != 64 && plan->block_m != 128)
         return fail(MEGA_MOE_ERR_INVALID_ARG, "plan block_m %d is not 32, 64 or 128", plan->block_m);
-    if (total_mb < 0) return fail(MEGA_MOE_ERR_INVALID_ARG, "total_mb < 0");
+    if (num_experts < 1) return fail(MEGA_MOE_ERR_INVALID_ARG, "num_experts < 1");
+    if (block_start[0] != 0) return fail(MEGA_MOE_ERR_INVALID_ARG, "block_start[0] != 0");
+    for (int e = 0; e < num_experts; ++e)
+        if (block_start[e + 1] < block_start[e])
+            return fail(MEGA_MOE_ERR_INVALID_ARG, "block_start decreases at expert %d", e);
     if (n_xcd < 1 || n_xcd > MAX_XCD)
         return fail(MEGA_MOE_ERR_INVALID_ARG, "n_xcd must be in [1, %d]", MAX_XCD);
     if (phase != 1 && phase != 2) return fail(MEGA_MOE_ERR_INVALID_ARG, "phase must be 1 or 2");
     const int nbs = phase == 1 ? plan->l1_n_blocks : plan->l2_n_blocks;
     if (nbs < 1) return fail(MEGA_MOE_ERR_INVALID_ARG, "plan has no N blocks for phase %d", phase);
+    const int total_mb = block_start[num_experts];
     if (total_mb > 0 && (!pb_out || !nb_out))
         return fail(MEGA_MOE_ERR_INVALID_ARG, "an output array is NULL");
+    std::vector<int> expert(total_mb);
+    for (int e = 0; e < num_experts; ++e)
+        for (int p = block_start[e]; p < block_start[e + 1]; ++p) expert[p] = e;
+    const auto expert_of = [&](int p) { return expert[p]; };
+    const auto start_of = [&](int e) { return (int)block_start[e]; };
     const int G = xcd_group_for(plan->block_m);
     int64_t i = 0;
     for (int x = 0; x < n_xcd; ++x) {
         int lo, cnt;
         xcd_range(total_mb, n_xcd, x, lo, cnt);
         for (int u = 0; u < cnt * nbs; ++u, ++i) {
-            int j, nb;
-            tile_coords(u, cnt, nbs, G, plan->l2_n_major != 0, j, nb);
-            pb_out[i] = lo + j;
+            int pb, nb;
+            tile_coords(u, lo, cnt, nbs, G, plan->l2_n_major != 0, expert_of, start_of, pb, nb);
+            pb_out[i] = pb;
             nb_out[i] = nb;
         }
     }

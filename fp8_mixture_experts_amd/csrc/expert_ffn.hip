@@ -999,10 +999,11 @@ moe_expert_ffn(MoeArgs a) {
         __syncthreads();
         if (u >= end) break;
         const bool is_l1 = u < l1_tiles;
-        int j, nb;
-        if (is_l1) tile_coords(u, cnt, a.nb1, G, a.n_major, j, nb);
-        else tile_coords(u - l1_tiles, cnt, a.nb2, G, a.n_major, j, nb);
-        const int pb = first + j;
+        const auto expert_of = [&](int p) { return __builtin_amdgcn_readfirstlane(a.pb_expert[p]); };
+        const auto block_start = [&](int e) { return __builtin_amdgcn_readfirstlane(a.mb_start[e]); };
+        int pb, nb;
+        if (is_l1) tile_coords(u, first, cnt, a.nb1, G, a.n_major, expert_of, block_start, pb, nb);
+        else tile_coords(u - l1_tiles, first, cnt, a.nb2, G, a.n_major, expert_of, block_start, pb, nb);
         const int e = __builtin_amdgcn_readfirstlane(a.pb_expert[pb]);
         const int m_local = pb - __builtin_amdgcn_readfirstlane(a.mb_start[e]);
         const int row0 = __builtin_amdgcn_readfirstlane(a.offsets[e]) + m_local * BM;

@@ -23,22 +23,33 @@ __host__ __device__ inline void xcd_range(int total_mb, int n_xcd, int x, int& l
     cnt = (int)((int64_t)total_mb * (x + 1) / n_xcd) - lo;
 }
 
-// Tile u of a range of cnt pool blocks x nbs N blocks: pool block j (relative
-// to the range) and N block nb.  Row-major keeps a pool block's N blocks
-// together; N-major runs each N block across the (at most G) pool blocks of a
-// group.
-__host__ __device__ inline void tile_coords(int u, int cnt, int nbs, int G, bool n_major, int& j,
-                                            int& nb) {
-    if (!n_major) {
-        j = u / nbs;
-        nb = u - j * nbs;
-        return;
+// Tile u of XCD range [first, first + cnt) with nbs N blocks: pool block pb
+// and N block nb.  The range's pool blocks form groups: each run of one
+// expert's blocks inside the range, cut into pieces of at most G blocks
+// (G = 1 when n_major is false).  Groups run in order, and a group's tiles
+// take each N block in turn over all of its pool blocks, so the tiles that
+// read one weight block run together and share it through the XCD's L2;
+// with G = 1 this is the row-major order.  A group of s blocks starting at
+// block g0 holds tiles [(g0 - first) * nbs, (g0 - first + s) * nbs), so
+// pool block first + u / nbs lies in the group of tile u.  expert_of(pb)
+// gives a pool block's expert and block_start(e) an expert's first pool
+// block (block_start(E) = the total).
+template <typename ExpertOf, typename BlockStart>
+__host__ __device__ inline void tile_coords(int u, int first, int cnt, int nbs, int G, bool n_major,
+                                            ExpertOf&& expert_of, BlockStart&& block_start,
+                                            int& pb, int& nb) {
+    const int pq = first + u / nbs;
+    int g0 = pq, s = 1;
+    if (n_major && G > 1) {
+        const int e = expert_of(pq);
+        const int r0 = max(block_start(e), first);
+        const int r1 = min(block_start(e + 1), first + cnt);
+        g0 = r0 + (pq - r0) / G * G;
+        s = min(G, r1 - g0);
     }
-    const int k = u / (G * nbs);
-    const int within = u - k * G * nbs;
-    const int g = min(G, cnt - k * G);
-    nb = within / g;
-    j = k * G + (within - nb * g);
+    const int within = u - (g0 - first) * nbs;
+    nb = within / s;
+    pb = g0 + (within - nb * s);
 }
 
 }  // namespace mega_moe

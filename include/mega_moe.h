@@ -192,20 +192,27 @@ int mega_moe_plan(const mega_moe_config* cfg, int32_t num_tokens, mega_moe_plan_
 
 /*
  * The expert kernel's tile order for a plan (a host-side query; needs no GPU).
- * The M pool blocks of a call are split into n_xcd contiguous ranges, XCD x
- * taking [x*M/n_xcd, (x+1)*M/n_xcd); that XCD's workgroups take the tiles of
- * its range from its own queue, all L1 tiles (phase 1) before the L2 tiles
- * (phase 2), each tile one pool block times one N block of plan->block_n
- * columns (SM90 design 12.2: N-major when plan->l2_n_major, else row-major).
- * Fills pb_out[i], nb_out[i] (host arrays of total_mb * N entries, N =
- * plan->l1_n_blocks or plan->l2_n_blocks) with the absolute pool block and N
+ * block_start[e] is expert e's first pool block, block_start[E] the number M
+ * of pool blocks (host array of num_experts + 1 non-decreasing entries from
+ * 0; a forward call's values are the mb_start view).  The M pool blocks are
+ * split into n_xcd contiguous ranges, XCD x taking [x*M/n_xcd,
+ * (x+1)*M/n_xcd); that XCD's workgroups take the tiles of its range from its
+ * own queue, all L1 tiles (phase 1) before the L2 tiles (phase 2), each tile
+ * one pool block times one N block of plan->block_n columns.  Row-major when
+ * plan->l2_n_major is 0.  N-major (SM90 design 12.2) otherwise, with groups
+ * aligned to experts: each run of one expert's pool blocks inside a range,
+ * cut into groups of at most 4 blocks (2 at block_m 64), takes every N block
+ * in turn over the group's blocks, so the tiles that read one weight block
+ * run together.  Fills pb_out[i], nb_out[i] (host arrays of M * N entries,
+ * N = plan->l1_n_blocks or plan->l2_n_blocks) with the pool block and N
  * block of the i-th tile: XCD 0's tiles in queue order, then XCD 1's, and so
- * on.  Returns MEGA_MOE_ERR_INVALID_ARG for a NULL plan or output, a block_m
- * other than 32/64/128, total_mb < 0, n_xcd outside [1, 16] or a phase other
- * than 1 or 2.
+ * on.  Returns MEGA_MOE_ERR_INVALID_ARG for a NULL argument, a block_m other
+ * than 32/64/128, num_experts < 1, a block_start that does not start at 0 or
+ * decreases, n_xcd outside [1, 16] or a phase other than 1 or 2.
  */
-int mega_moe_tile_order(const mega_moe_plan_info* plan, int32_t total_mb, int32_t n_xcd,
-                        int32_t phase, int32_t* pb_out, int32_t* nb_out);
+int mega_moe_tile_order(const mega_moe_plan_info* plan, int32_t num_experts,
+                        const int32_t* block_start, int32_t n_xcd, int32_t phase,
+                        int32_t* pb_out, int32_t* nb_out);
 
 /*
  * Device views of the intermediates of the last forward call (the buffer views

@@ -138,44 +138,59 @@ def test_transform_rejects_bad_arguments():
     assert ei.value.code == B.MEGA_MOE_ERR_INVALID_ARG
 
 
+def _layouts():
+    # expert pool-block counts: empty, single blocks, runs longer than a
+    # group, zero-block experts, and one huge expert
+    rng = __import__("numpy").random.default_rng(5)
+    yield [0]
+    yield [1]
+    yield [3, 0, 1, 9, 2, 0, 0, 5]
+    yield list(rng.integers(0, 4, 32))
+    yield list(rng.integers(0, 12, 64))
+    yield [63] + list(rng.integers(1, 20, 29))
+
+
 @pytest.mark.parametrize("bm,nm,bn", [(32, 0, 128), (32, 1, 128), (64, 0, 128), (64, 1, 256),
                                       (128, 0, 256), (128, 1, 128)])
-@pytest.mark.parametrize("total_mb", [0, 1, 3, 7, 8, 9, 23, 64, 515])
 @pytest.mark.parametrize("n_xcd", [1, 3, 8])
-def test_tile_order_visits_every_tile_once(bm, nm, bn, total_mb, n_xcd):
+def test_tile_order_visits_every_tile_once(bm, nm, bn, n_xcd):
     # every (pool block, N block) of each phase exactly once; each XCD stays
-    # within its contiguous range of pool blocks; N-major groups run an N
-    # block across their pool blocks before the next N block
+    # within its contiguous range of pool blocks; N-major groups are runs of
+    # one expert's blocks inside a range, at most G long, and take each N
+    # block over their blocks before the next N block
     plan = B.mega_moe_plan(_cfg(block_m=bm, l2_n_major=nm, block_n=bn), 4096)
     assert (plan.block_m, plan.l2_n_major, plan.block_n) == (bm, nm, bn)
-    group = 2 if bm == 64 else 4
-    for phase, nbs in ((1, plan.l1_n_blocks), (2, plan.l2_n_blocks)):
-        pb, nb = B.mega_moe_tile_order(plan, total_mb, n_xcd, phase)
-        pairs = list(zip(pb, nb))
-        assert sorted(pairs) == [(p, n) for p in range(total_mb) for n in range(nbs)]
-        i = 0
-        for x in range(n_xcd):
-            lo, hi = total_mb * x // n_xcd, total_mb * (x + 1) // n_xcd
-            mine = pairs[i:i + (hi - lo) * nbs]
-            i += (hi - lo) * nbs
-            assert all(lo <= p < hi for p, _ in mine)
-            if not nm:
-                assert mine == [(p, n) for p in range(lo, hi) for n in range(nbs)]
-            else:
-                want = []
-                for g0 in range(lo, hi, group):
-                    members = range(g0, min(g0 + group, hi))
-                    want += [(p, n) for n in range(nbs) for p in members]
-                assert mine == want
-        assert i == len(pairs)
+    G = (2 if bm == 64 else 4) if nm else 1
+    for counts in _layouts():
+        starts = [0]
+        for c in counts:
+            starts.append(starts[-1] + int(c))
+        M = starts[-1]
+        expert = [e for e, c in enumerate(counts) for _ in range(int(c))]
+        for phase, nbs in ((1, plan.l1_n_blocks), (2, plan.l2_n_blocks)):
+            pb, nb = B.mega_moe_tile_order(plan, starts, n_xcd, phase)
+            pairs = list(zip(pb, nb))
+            assert sorted(pairs) == [(p, n) for p in range(M) for n in range(nbs)]
+            want = []
+            for x in range(n_xcd):
+                lo, hi = M * x // n_xcd, M * (x + 1) // n_xcd
+                p = lo
+                while p < hi:
+                    q = p
+                    while q < hi and q - p < G and expert[q] == expert[p]:
+                        q += 1
+                    want += [(r, n) for n in range(nbs) for r in range(p, q)]
+                    p = q
+            assert pairs == want
 
 
 def test_tile_order_rejects_bad_arguments():
     plan = B.mega_moe_plan(_cfg(), 128)
-    for args in ((-1, 8, 1), (4, 0, 1), (4, 17, 1), (4, 8, 3)):
+    for starts, n_xcd, phase in (([0, 4], 0, 1), ([0, 4], 17, 1), ([0, 4], 8, 3),
+                                 ([1, 4], 8, 1), ([0, 4, 2], 8, 1)):
         with pytest.raises(B.MegaMoEError) as ei:
-            B.mega_moe_tile_order(plan, *args)
+            B.mega_moe_tile_order(plan, starts, n_xcd, phase)
         assert ei.value.code == B.MEGA_MOE_ERR_INVALID_ARG
     plan.block_m = 48
     with pytest.raises(B.MegaMoEError):
-        B.mega_moe_tile_order(plan, 4, 8, 1)
+        B.mega_moe_tile_order(plan, [0, 4], 8, 1)
