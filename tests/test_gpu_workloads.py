@@ -1,5 +1,6 @@
 """GPU parity at the full sizes of the benchmark workloads, in the launch
-configuration the benchmark times (the default plan).
+configuration the benchmark times (the default plan), with FP8 weights and,
+for mid and prefill, MXFP4 weights.
 
 At these sizes the whole dispatch (counts, offsets, slot map, source rows) and
 the pool copies are checked bit-exactly against the oracle's dispatch, and a
@@ -17,15 +18,14 @@ from tests import gpu_util as G
 
 pytestmark = pytest.mark.gpu
 
-WORKLOADS = ["decode", "mid", "wide", "prefill"]
+WORKLOADS = ["decode", "mid", "wide", "prefill", "mid_mxfp4", "prefill_mxfp4"]
 
 
 @pytest.mark.parametrize("name", WORKLOADS)
 def test_full_size_workload(name):
     inp = S.make_inputs(name)
     T, H = inp["x"].shape
-    k = inp["topk_idx"].shape[1]
-    E = inp["w1"].shape[0]
+    E, _, _, k = G.layer_dims(inp)
     print(f"[{name}] T={T} H={H} E={E} k={k}", flush=True)
     run = G.Runner(inp, keep_pool=1)
     try:
