@@ -102,7 +102,10 @@ int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out);
 
 /*
  * One forward pass of the layer, asynchronous on `stream` (no host
- * synchronisation, no allocation).  Shapes (T = num_tokens):
+ * synchronisation, no allocation, no memory sets: every counter it uses is
+ * reset by its own kernels, so a call may be captured in a HIP graph and the
+ * graph replayed; the split phases, split_l2_cus > 0, fork to streams of
+ * their own and are not meant for capture).  Shapes (T = num_tokens):
  *   x            [T, H]            uint8 E4M3 activations
  *   x_sf         [T, H/128]        float scale per token per 128 channels
  *   topk_idx     [T, k]            int32 expert of each slot; < 0 = inactive

@@ -82,7 +82,10 @@ class Runner:
         self.layer = B.MegaMoE(E, H, I, k, max_tokens if max_tokens is not None else T, **cfg)
         self.dev = to_device(inp)
 
-    def forward(self, dev=None, num_tokens=None):
+    def forward(self, dev=None, num_tokens=None, sync=True):
+        """One forward on torch's current stream; with sync, waits for it and
+        returns the device error bits (sync=False launches only, as under
+        graph capture)."""
         d = dev or self.dev
         T = d["x"].shape[0] if num_tokens is None else num_tokens
         stream = torch.cuda.current_stream().cuda_stream
@@ -94,8 +97,12 @@ class Runner:
             B.mega_moe_forward(self.layer.handle, T, d["x"], d["x_sf"], d["topk_idx"],
                                d["topk_weights"], d["w1"], d["w1_sf"], d["w2"], d["w2_sf"],
                                d["y"], stream)
-        status = self.layer.status()
-        return status
+        if not sync:
+            return None
+        return self.layer.status()
+
+    def clear_y(self, dev=None):
+        (dev or self.dev)["y"].zero_()
 
     def y(self, dev=None):
         d = dev or self.dev
