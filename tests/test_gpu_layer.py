@@ -176,6 +176,14 @@ EDGE = {
                                        weight_seed=46),
     "one_token": S.custom("one_token", tokens=1, hidden=512, intermediate=256, experts=8,
                           topk=2, seed=47, weight_seed=48),
+    # the largest expert count (one expert per dispatch scan thread), most
+    # experts with a handful of routes or none: 2400 routes take the
+    # one-workgroup dispatch, 4800 the chunked one
+    "max_experts_small": S.custom("max_experts_small", tokens=300, hidden=128, intermediate=128,
+                                  experts=1024, topk=8, seed=349, weight_seed=50),
+    "max_experts_chunked": S.custom("max_experts_chunked", tokens=600, hidden=128,
+                                    intermediate=128, experts=1024, topk=8, seed=649,
+                                    weight_seed=50),
 }
 
 
