@@ -111,7 +111,8 @@ def cpu_baseline(name, inp, work):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 50, or 20 for the prefill workloads)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--block-m", type=int, default=0)
@@ -136,6 +137,8 @@ def main():
     from fp8_mixture_experts_amd import rocprof_summary as RS
 
     name = args.workload
+    if args.steps is None:
+        args.steps = 20 if name.startswith("prefill") else 50
     inp = S.make_inputs(name)
     work = work_of(inp)
     wkeys = ("w1_fp4", "w1_e8", "w2_fp4", "w2_e8") if work["mx"] else ("w1", "w1_sf", "w2", "w2_sf")
