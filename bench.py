@@ -112,8 +112,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 50, or 20 for the prefill workloads)")
-    ap.add_argument("--warmup", type=int, default=5)
+                    help="timed steps (default 200, or 20 for the prefill workloads: "
+                         "about 60 ms and 110 ms of GPU time, long enough for steady state)")
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--block-n", type=int, default=0)
@@ -138,7 +139,7 @@ def main():
 
     name = args.workload
     if args.steps is None:
-        args.steps = 20 if name.startswith("prefill") else 50
+        args.steps = 20 if name.startswith("prefill") else 200
     inp = S.make_inputs(name)
     work = work_of(inp)
     wkeys = ("w1_fp4", "w1_e8", "w2_fp4", "w2_e8") if work["mx"] else ("w1", "w1_sf", "w2", "w2_sf")
