@@ -114,7 +114,7 @@ def main():
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default 200, or 20 for the prefill workloads: "
                          "about 60 ms and 110 ms of GPU time, long enough for steady state)")
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--block-n", type=int, default=0)
