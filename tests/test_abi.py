@@ -50,11 +50,11 @@ def test_plan_matches_golden_tiers():
     rows = [l.split() for l in open(os.path.join(ROOT, "tests/golden/block_m_tiers.txt"))
             if l.strip() and not l.startswith("#")]
     assert len(rows) >= 10
-    for t, k, e, exp, bm, nm in rows:
+    for t, k, e, exp, bm, nm, bn in rows:
         cfg = _cfg(num_experts=int(e), num_topk=int(k), max_tokens=max(int(t), 1))
         p = B.mega_moe_plan(cfg, int(t))
         assert math.isclose(p.expected_tokens_per_expert, float(exp), rel_tol=1e-6)
-        assert (p.block_m, p.l2_n_major) == (int(bm), int(nm)), (t, k, e)
+        assert (p.block_m, p.l2_n_major, p.block_n) == (int(bm), int(nm), int(bn)), (t, k, e)
         assert p.l1_n_blocks == 2 * 2048 // p.block_n and p.l2_n_blocks == 7168 // p.block_n
 
 
@@ -63,6 +63,15 @@ def test_plan_matches_golden_tiers():
 def test_activation_options_are_accepted(kw):
     assert B.mega_moe_workspace_bytes(_cfg(**kw)) > 0
     B.mega_moe_plan(_cfg(**kw), 128)
+
+
+def test_plan_keeps_128_columns_where_256_do_not_fit():
+    # 64-row tiles go 256 wide only when H splits into 256-column tiles (2I
+    # always does: I is a multiple of 128)
+    assert B.mega_moe_plan(_cfg(hidden=7296), 128).block_n == 128       # H = 57 x 128
+    assert B.mega_moe_plan(_cfg(intermediate=2176), 128).block_n == 256  # 2I = 17 x 256
+    assert B.mega_moe_plan(_cfg(), 128).block_n == 256
+    assert B.mega_moe_plan(_cfg(), 4096).block_n == 128                  # 128-row tiles
 
 
 def test_plan_overrides():
