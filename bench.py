@@ -9,17 +9,25 @@ HBM.  Prints one JSON line.  The default workload is the 128-token decode
 batch (hidden 7168, intermediate 2048, 32 local experts, top-8, uniform
 routing), which is weight-stream bound: ``value`` is the achieved
 weight-stream rate (bytes of the active experts' FP8 weights and scales per
-step / step time); the prefill workload reports FP8 TFLOP/s instead.
+step / step time); the prefill workload reports FP8 TFLOP/s instead.  With
+the decode workload the line also carries ``prefill``: the same measurement
+of the 8192-token prefill batch (Zipf(1.2) routing), the compute-bound half
+of the metric, in the same process with the same step counts.
 
-The K timed steps run twice.  The first pass is plain: its wall time,
-bracketed by device synchronisations, gives ``ms_per_step`` and ``value``.
-The second pass records HIP events on the layer's stream around each kernel
-group of every step; these per-launch durations give ``kernel_ms`` and the
-``roofline`` of the dominant kernel (the persistent expert kernel).  The
-events add a few microseconds per step, which is why they stay out of the
-first pass.  The algorithmic bytes and FLOPs per launch are computed below.
-``cpu_baseline`` times the float64 CPU oracle on this host on a bounded sample
-of the same workload.
+W untimed warm-up steps, then the K timed steps, twice.  The first pass is
+plain: its wall time, bracketed by device synchronisations, gives
+``ms_per_step`` and ``value``.  The second pass records HIP events on the
+layer's stream around each kernel group of every step; these per-launch
+durations give ``kernel_ms`` and the ``roofline`` of the dominant kernel (the
+persistent expert kernel).  The events add a few microseconds per step,
+which is why they stay out of the first pass.  ``roofline.achieved`` is the
+algorithmic work per launch over the expert kernel's mean event time: the
+compulsory bytes (the active experts' weights and scales, x and its scales,
+the top-k ids and weights, y) for the HBM-bound workloads, 6*H*I FLOPs per
+route for prefill.  The intermediates the method writes and reads back
+(re-quantised activations, BF16 partials) are reported beside it, not
+counted.  ``cpu_baseline`` times the float64 CPU oracle on this host on a
+bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -57,13 +65,16 @@ def work_of(inp):
     else:
         w_bytes = active_experts * (3.0 * H * I + 4.0 * (2 * I // 128) * (H // 128)
                                     + 4.0 * (H // 128) * (I // 128))
+    # compulsory bytes: the active experts' weights and scales, x and its
+    # scales, the top-k ids and weights, y
     io_bytes = T * H + 4.0 * T * (H // 128) + 8.0 * T * k + 2.0 * T * H
-    # the expert kernel: weights + pool rows and scales in, re-quantised
-    # activations out and back in, BF16 partials out
-    route_bytes = H + 4.0 * (H // 128) + 4 + 2.0 * (I + 4.0 * (I // 64)) + 2.0 * H
+    # intermediates the method itself writes and reads back (not part of the
+    # roofline, reported beside it): re-quantised activations and their
+    # scales, BF16 partials
+    inter_bytes = R * (2.0 * (I + 4.0 * (I // 64)) + 2.0 * 2.0 * H)
     return dict(T=T, H=H, I=I, E=E, k=k, R=R, active_experts=active_experts, flops=flops, mx=mx,
                 weight_bytes=w_bytes, compulsory_bytes=w_bytes + io_bytes,
-                expert_kernel_bytes=w_bytes + R * route_bytes)
+                intermediate_bytes=inter_bytes)
 
 
 def _blas_threads():
@@ -84,13 +95,14 @@ def cpu_baseline(name, inp, work):
     cores = _blas_threads()
     T = inp["x"].shape[0]
     if T <= 128:
-        # whole forwards, repeated until about 10 s of CPU work
-        reps, t0 = 0, time.perf_counter()
-        while reps < 8 and (reps == 0 or time.perf_counter() - t0 < 10.0):
+        # whole forwards, best of 3 (about 10 s of CPU work at the decode size)
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
             moe.forward(inp)
-            reps += 1
-        dt = (time.perf_counter() - t0) / reps
-        sample = f"full {name} workload ({T} tokens), mean of {reps} forwards"
+            times.append(time.perf_counter() - t0)
+        dt = min(times)
+        sample = f"full {name} workload ({T} tokens), best of 3 forwards"
         frac = 1.0
     else:
         n = 64
@@ -108,38 +120,15 @@ def cpu_baseline(name, inp, work):
             "seconds": dt, "blas": "numpy float64"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 200, or 20 for the prefill workloads: "
-                         "about 60 ms and 110 ms of GPU time, long enough for steady state)")
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="decode")
-    ap.add_argument("--block-m", type=int, default=0)
-    ap.add_argument("--block-n", type=int, default=0)
-    ap.add_argument("--l2-n-major", type=int, default=-1)
-    ap.add_argument("--split-l2-cus", type=int, default=0,
-                    help="run L1 and L2 tiles as two concurrent kernels, the L2 one with this "
-                         "many CUs' worth of workgroups per XCD (0: one fused kernel)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="after the timed steps, run one plain device copy of this many MiB "
-                         "(calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (the layer is one GPU's share of expert "
-              f"parallelism; no multi-GPU path is built); got --gpus {args.gpus}", file=sys.stderr)
-        sys.exit(2)
+# With L1 on the exact F16 matrix path (two thirds of the FLOPs at the F16
+# rate, 2.5 PFLOP/s) and L2 on FP8 (one third at 5.0 PFLOP/s), the layer's own
+# ceiling at full MFMA use is 1 / (2/3 / 2.5 + 1/3 / 5.0) = 3.0 PFLOP/s.
+EXACT_PATH_PEAK_TFLOPS = 1.0 / ((2.0 / 3.0) / 2500.0 + (1.0 / 3.0) / 5000.0)
 
-    import torch
-    from fp8_mixture_experts_amd import binding as B
-    from fp8_mixture_experts_amd import synthetic as S
-    from fp8_mixture_experts_amd import rocprof_summary as RS
 
-    name = args.workload
-    if args.steps is None:
-        args.steps = 20 if name.startswith("prefill") else 200
+def measure(name, args, torch, B, S, RS):
+    """Times `args.steps` forwards of one workload after `args.warmup`
+    untimed ones; returns (inputs, work, result dict)."""
     inp = S.make_inputs(name)
     work = work_of(inp)
     wkeys = ("w1_fp4", "w1_e8", "w2_fp4", "w2_e8") if work["mx"] else ("w1", "w1_sf", "w2", "w2_sf")
@@ -151,7 +140,6 @@ def main():
                       block_n=args.block_n, l2_n_major=args.l2_n_major,
                       split_l2_cus=args.split_l2_cus)
     plan = B.mega_moe_plan(layer.cfg, T)
-
     fwd = layer.forward_mxfp4 if work["mx"] else layer.forward
 
     def step():
@@ -162,7 +150,7 @@ def main():
         step()
     status = layer.status()
     if status:
-        raise SystemExit(f"device error bits {status:#x}")
+        raise SystemExit(f"{name}: device error bits {status:#x}")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -178,18 +166,11 @@ def main():
     torch.cuda.synchronize()
     t3 = time.perf_counter()
     prof = B.mega_moe_profile_end(layer.handle, args.steps)
-    if args.copy_probe_mib > 0:
-        n = args.copy_probe_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     status = layer.status()
     if status:
-        raise SystemExit(f"device error bits {status:#x}")
+        raise SystemExit(f"{name}: device error bits {status:#x}")
     layer.close()
+    del dev, y
 
     ms = (t1 - t0) * 1e3 / args.steps
     s = ms / 1e3
@@ -204,22 +185,24 @@ def main():
                 "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
     else:
         value, unit = wgbs, "GB/s"
-        roof = {"bound": "hbm", "achieved": work["expert_kernel_bytes"] / (expert_ms / 1e3) / 1e9,
+        roof = {"bound": "hbm", "achieved": work["compulsory_bytes"] / (expert_ms / 1e3) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     # calibrated HBM bytes per launch from the committed counter summary of
     # this workload; None when the library sources changed since it was taken
     roof["traffic"] = RS.read_traffic(
         os.path.join(ROOT, "profiles", f"moe_expert_ffn_{name}_hbm_traffic.txt"), name)
-    roof["algorithmic_bytes"] = work["expert_kernel_bytes"]
+    roof["algorithmic_bytes"] = work["compulsory_bytes"]
+    roof["algorithmic_flops"] = work["flops"]
+    roof["intermediate_bytes"] = work["intermediate_bytes"]
+    if roof["bound"] == "mfma":
+        roof["exact_path_peak"] = EXACT_PATH_PEAK_TFLOPS
+        roof["frac_of_exact_path_peak"] = roof["achieved"] / EXACT_PATH_PEAK_TFLOPS
     roof["kernel"] = (f"moe_expert_ffn<{plan.block_m}x128, mxfp4>" if work["mx"]
                       else f"moe_expert_ffn<{plan.block_m}x{plan.block_n}>")
     roof["kernel_ms"] = expert_ms
-    out = {
-        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8_e4m3 x mxfp4" if work["mx"] else "fp8_e4m3",
-        "data": "synthetic",
+    res = {
+        "value": value, "unit": unit, "ms_per_step": ms,
         "config": {"workload": name, "tokens": T, "hidden": H, "intermediate": work["I"],
                    "experts": work["E"], "topk": work["k"], "routing": inp["workload"].routing,
                    "block_m": plan.block_m, "block_n": 128 if work["mx"] else plan.block_n,
@@ -238,7 +221,62 @@ def main():
         "ms_per_step_with_events": (t3 - t2) * 1e3 / args.steps,
         "roofline": roof,
     }
+    return inp, work, res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20,
+                    help="timed steps of each workload")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--block-n", type=int, default=0)
+    ap.add_argument("--l2-n-major", type=int, default=-1)
+    ap.add_argument("--split-l2-cus", type=int, default=0,
+                    help="run L1 and L2 tiles as two concurrent kernels, the L2 one with this "
+                         "many CUs' worth of workgroups per XCD (0: one fused kernel)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="with the decode workload, skip the prefill measurement that the "
+                         "line otherwise carries under \"prefill\"")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many MiB "
+                         "(calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the layer is one GPU's share of expert "
+              f"parallelism; no multi-GPU path is built); got --gpus {args.gpus}", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from fp8_mixture_experts_amd import binding as B
+    from fp8_mixture_experts_amd import synthetic as S
+    from fp8_mixture_experts_amd import rocprof_summary as RS
+
+    name = args.workload
+    inp, work, res = measure(name, args, torch, B, S, RS)
+    out = {
+        "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3 x mxfp4" if work["mx"] else "fp8_e4m3", "data": "synthetic",
+    }
+    out.update({k: v for k, v in res.items() if k not in ("value", "unit", "ms_per_step")})
+    if name == "decode" and not args.no_prefill:
+        # the compute-bound half of the metric: the 8192-token prefill batch,
+        # the same number of warm-up and timed steps
+        _, _, pre = measure("prefill", args, torch, B, S, RS)
+        out["prefill"] = pre
     if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
         out["copy_probe_bytes"] = args.copy_probe_mib << 20
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(name, inp, work)

@@ -31,7 +31,7 @@ EXPORTS = ["mega_moe_create", "mega_moe_forward", "mega_moe_forward_mxfp4", "meg
            "mega_moe_last_error", "mega_moe_workspace_bytes", "mega_moe_token_alignment",
            "mega_moe_plan", "mega_moe_tile_order", "mega_moe_get_views", "mega_moe_set_recv_stats",
            "mega_moe_transform_w1", "mega_moe_profile_begin",
-           "mega_moe_profile_end"]
+           "mega_moe_profile_end", "mega_moe_check_xcd_layout"]
 
 
 class mega_moe_config(ctypes.Structure):
@@ -104,6 +104,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mega_moe_profile_end.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32,
                                          ctypes.POINTER(i32)]
     lib.mega_moe_profile_end.restype = ctypes.c_int
+    lib.mega_moe_check_xcd_layout.argtypes = [i32, i32, ctypes.c_uint32]
+    lib.mega_moe_check_xcd_layout.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -164,6 +166,10 @@ def mega_moe_get_status(handle, stream) -> int:
 
 def mega_moe_last_error() -> str:
     return load().mega_moe_last_error().decode()
+
+
+def mega_moe_check_xcd_layout(num_xcds: int, num_cus: int, seen_ids: int = 0) -> int:
+    return _check(load().mega_moe_check_xcd_layout(num_xcds, num_cus, seen_ids))
 
 
 def mega_moe_workspace_bytes(cfg: mega_moe_config) -> int:

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libmega_moe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["dispatch.hip", "expert_ffn.hip", "combine.hip", "transform.hip", "api.cpp"]
+SOURCES = ["dispatch.hip", "expert_ffn.hip", "combine.hip", "transform.hip", "api.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-result"]

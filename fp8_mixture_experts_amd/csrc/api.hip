@@ -18,6 +18,7 @@ namespace mega_moe {
 void launch_dispatch(const MoeArgs& a, int gather_blocks, hipStream_t stream);
 int launch_expert_ffn(const MoeArgs& a, int num_cus, hipStream_t stream);
 void launch_combine(const MoeArgs& a, hipStream_t stream);
+hipError_t probe_xcds(uint32_t* word, int num_cus, uint32_t* seen);
 void launch_transform_w1(const uint8_t* w1, const float* sf, uint8_t* out, float* out_sf, int E,
                          int N, int H, hipStream_t stream);
 }  // namespace mega_moe
@@ -126,9 +127,11 @@ Layout make_layout(const mega_moe_config& c) {
     sz[L_SRC] = L.P_cap * 4;
     sz[L_CHIST] = L.chunks_max * E * 4;
     sz[L_CBASE] = L.chunks_max * E * 4;
-    sz[L_L1ACTS] = L.P_cap * H;
-    sz[L_L1SF] = (H / 128) * L.P_cap * 4;
-    sz[L_L1W] = L.P_cap * 4;
+    // the pool copies exist only when the configuration keeps the pool
+    const int64_t pool_rows = c.keep_pool ? L.P_cap : 0;
+    sz[L_L1ACTS] = pool_rows * H;
+    sz[L_L1SF] = (H / 128) * pool_rows * 4;
+    sz[L_L1W] = pool_rows * 4;
     sz[L_L2ACTS] = L.P_cap * I;
     sz[L_L2SF] = (I / 64) * L.P_cap * 4;
     sz[L_COMB] = L.R_max * H * 2;
@@ -174,6 +177,23 @@ void plan(const mega_moe_config& c, int32_t T, mega_moe_plan_info* p) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// XCDs (accelerator dies, each with its own L2) of device dev.  The expert
+// kernel keeps one work queue per XCD so that the L1 tiles of a pool block
+// and the L2 tiles that read their output run on one XCD and meet in its L2
+// without any cache write-back; that needs the device's XCD count, and its
+// compute units must split evenly over them.
+int xcd_count(int dev, int num_cus, int* out) {
+    int n = 0;
+    hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev);
+    if (e != hipSuccess)
+        return fail(MEGA_MOE_ERR_UNSUPPORTED, "XCD count of device %d unknown: %s", dev,
+                    hipGetErrorString(e));
+    const int rc = mega_moe_check_xcd_layout(n, num_cus, 0);
+    if (rc) return rc;
+    *out = n;
+    return MEGA_MOE_OK;
+}
+
 }  // namespace
 
 struct mega_moe_handle {
@@ -181,6 +201,7 @@ struct mega_moe_handle {
     Layout L;
     int device;
     int num_cus;
+    int n_xcd;
     uint8_t* ws;
     int32_t last_T;
     MoeArgs base;   // workspace pointers and sizes filled at create
@@ -246,6 +267,24 @@ int split_setup(mega_moe_handle* h, int l2) {
 extern "C" {
 
 const char* mega_moe_last_error(void) { return g_last_error.c_str(); }
+
+int mega_moe_check_xcd_layout(int32_t num_xcds, int32_t num_cus, uint32_t seen_ids) {
+    if (num_xcds < 1 || num_xcds > MAX_XCD || num_cus < 1 || num_cus % num_xcds != 0)
+        return fail(MEGA_MOE_ERR_UNSUPPORTED,
+                    "device reports %d XCDs for %d compute units; the expert kernel needs 1..%d "
+                    "XCDs with the same number of compute units each", num_xcds, num_cus, MAX_XCD);
+    if (seen_ids == 0) return ok();
+    // the kernel takes XCD id % num_xcds as its queue: the ids must give
+    // num_xcds distinct queues
+    uint32_t queues = 0;
+    for (int i = 0; i < 32; ++i)
+        if (seen_ids >> i & 1u) queues |= 1u << (i % num_xcds);
+    if (__builtin_popcount(seen_ids) != num_xcds || __builtin_popcount(queues) != num_xcds)
+        return fail(MEGA_MOE_ERR_UNSUPPORTED,
+                    "workgroups report the XCD ids of mask %#x on a device of %d XCDs: the "
+                    "L1 -> L2 handoff needs one work queue per XCD", seen_ids, num_xcds);
+    return ok();
+}
 
 int32_t mega_moe_token_alignment(void) { return POOL_ALIGN; }
 
@@ -317,11 +356,15 @@ int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out) {
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
         return fail(MEGA_MOE_ERR_UNSUPPORTED, "device %d is %s, this library is built for gfx950",
                     dev, prop.gcnArchName);
+    int n_xcd = 0;
+    rc = xcd_count(dev, prop.multiProcessorCount, &n_xcd);
+    if (rc) return rc;
     auto* h = new mega_moe_handle{};
     h->cfg = *cfg;
     h->L = make_layout(*cfg);
     h->device = dev;
     h->num_cus = prop.multiProcessorCount;
+    h->n_xcd = n_xcd;
     e = hipMalloc((void**)&h->ws, h->L.total);
     if (e != hipSuccess) {
         const long long bytes = (long long)h->L.total;
@@ -335,6 +378,25 @@ int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out) {
         delete h;
         return fail(MEGA_MOE_ERR_HIP, "workspace clear: %s", hipGetErrorString(e));
     }
+    // the expert kernel's L1 -> L2 handoff relies on every workgroup reading
+    // its own XCD from the hardware: check that the device's workgroups report
+    // exactly n_xcd distinct XCDs (the control record serves as the probe's word)
+    uint32_t seen = 0;
+    e = probe_xcds(reinterpret_cast<uint32_t*>(h->ws + h->L.off[L_CTRL]), h->num_cus, &seen);
+    if (e == hipSuccess) e = hipMemset(h->ws + h->L.off[L_CTRL], 0, sizeof(MoeCtrl));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        hipFree(h->ws);
+        delete h;
+        return fail(MEGA_MOE_ERR_HIP, "XCD probe: %s", hipGetErrorString(e));
+    }
+    rc = mega_moe_check_xcd_layout(n_xcd, h->num_cus, seen);
+    if (rc) {
+        const std::string msg = g_last_error;
+        hipFree(h->ws);
+        delete h;
+        return fail(rc, "%s", msg.c_str());
+    }
     MoeArgs& a = h->base;
     std::memset(&a, 0, sizeof a);
     const Layout& L = h->L;
@@ -346,9 +408,7 @@ int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out) {
     a.wait_spin_limit = 1u << 20;
     a.act_clamp = cfg->activation_clamp;
     a.fast_math = cfg->fast_math;
-    // gfx950 groups 32 compute units per XCD, each XCD with its own L2
-    a.n_xcd = (h->num_cus % 32 == 0 && h->num_cus / 32 >= 1 && h->num_cus / 32 <= MAX_XCD)
-                  ? h->num_cus / 32 : 1;
+    a.n_xcd = h->n_xcd;
     uint8_t* w = h->ws;
     a.counts = (int32_t*)(w + L.off[L_COUNTS]);
     a.offsets = (int32_t*)(w + L.off[L_OFFSETS]);
@@ -586,9 +646,10 @@ int mega_moe_get_views(mega_moe_handle* h, mega_moe_views* v) {
     v->offsets = a.offsets;
     v->slot_map = a.slot_map;
     v->src = a.src;
-    v->l1_acts = a.l1_acts;
-    v->l1_acts_sf = a.l1_sf;
-    v->l1_topk_weights = a.l1_w;
+    const bool pool = h->cfg.keep_pool != 0;
+    v->l1_acts = pool ? a.l1_acts : nullptr;
+    v->l1_acts_sf = pool ? a.l1_sf : nullptr;
+    v->l1_topk_weights = pool ? a.l1_w : nullptr;
     v->l2_acts = a.l2_acts;
     v->l2_acts_sf = a.l2_sf;
     v->combine_buf = a.comb;

@@ -808,7 +808,14 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
         m = fmaxf(m, dpp_move<0xB1>(m));                                // quad_perm [1,0,3,2]
         m = fmaxf(m, dpp_move<0x4E>(m));                                // quad_perm [2,3,0,1]
         const float sf = m / 448.0f;
-        const float inv = sf > 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
+        // h * (1 / sf); below 2^-100 (a row whose top-k weight underflowed,
+        // say) h and sf are first scaled by 2^100, exactly, so that the
+        // reciprocal stays finite; sf = 0 (amax = 0, or amax / 448 below the
+        // smallest float) gives codes of zero
+        const float up = sf < 0x1p-100f ? 0x1p100f : 1.0f;
+        const float inv = sf > 0.0f ? __builtin_amdgcn_rcpf(sf * up) : 0.0f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) hv[q] *= up;
         uint32_t code[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1027,6 +1034,24 @@ static int launch_one(const MoeArgs& a, int num_cus, hipStream_t stream) {
     }
     hipLaunchKernelGGL((moe_expert_ffn<MS, BNT, WF>), dim3(num_cus * per_cu), dim3(NT), 0, stream, a);
     return num_cus * per_cu;
+}
+
+// Every workgroup sets bit XCC_ID of *word: the XCD ids the device's
+// workgroups run on (checked once when a handle is created).
+__global__ void __launch_bounds__(64) moe_xcd_probe(uint32_t* word) {
+    if (threadIdx.x == 0)
+        atomicOr(word, 1u << (__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xf));
+}
+
+// Runs the probe over 4 workgroups per compute unit (workgroups are dealt to
+// the XCDs in turn, so every XCD gets some) and returns the mask in *seen.
+hipError_t probe_xcds(uint32_t* word, int num_cus, uint32_t* seen) {
+    hipError_t e = hipMemset(word, 0, sizeof(uint32_t));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(moe_xcd_probe, dim3(4 * num_cus), dim3(64), 0, nullptr, word);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return hipMemcpy(seen, word, sizeof(uint32_t), hipMemcpyDeviceToHost);
 }
 
 int launch_expert_ffn(const MoeArgs& a, int num_cus, hipStream_t stream) {

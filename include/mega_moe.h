@@ -94,9 +94,12 @@ typedef struct mega_moe_handle mega_moe_handle;
 
 /*
  * Validates cfg (H % 128 == 0, I % 128 == 0, k >= 1, E >= 1, unsupported
- * options rejected) on the current HIP device, checks that it is gfx950, and
- * allocates the handle-owned workspace for max_tokens (pool, re-quantised
- * activations, BF16 partials, counters, metadata).  *out is set to NULL on error.
+ * options rejected) on the current HIP device, checks that it is gfx950 and
+ * that its XCDs pass mega_moe_check_xcd_layout (with the XCD ids a small
+ * probe kernel reports; UNSUPPORTED otherwise), and allocates the
+ * handle-owned workspace for max_tokens (re-quantised activations, BF16
+ * partials, counters, metadata; the pool copies only with keep_pool).
+ * Synchronises the device.  *out is set to NULL on error.
  */
 int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out);
 
@@ -168,6 +171,19 @@ int mega_moe_get_status(mega_moe_handle* h, void* stream);
 /* Message for the last non-zero return on the calling thread ("" if none). */
 const char* mega_moe_last_error(void);
 
+/*
+ * The device check mega_moe_create applies (host-only; needs no GPU).  The
+ * expert kernel keeps one work queue per XCD (accelerator die with its own
+ * L2), so the L1 tiles of a pool block and the L2 tiles that read their
+ * output run on one XCD and meet in its L2 (the single-GPU form of the L2
+ * arrival mask handoff, SM90 design 14.3).  MEGA_MOE_OK when num_xcds is in
+ * 1..16 and divides num_cus and, if seen_ids is non-zero (a mask of the XCD
+ * ids workgroups reported, bit i for id i), the ids number num_xcds and fall
+ * into num_xcds distinct queues (id % num_xcds); MEGA_MOE_ERR_UNSUPPORTED
+ * otherwise.
+ */
+int mega_moe_check_xcd_layout(int32_t num_xcds, int32_t num_cus, uint32_t seen_ids);
+
 /* Workspace bytes mega_moe_create would allocate for cfg (-1 if invalid).
  * Host-only; needs no GPU. */
 int64_t mega_moe_workspace_bytes(const mega_moe_config* cfg);
@@ -227,10 +243,11 @@ typedef struct mega_moe_views {
     int32_t* offsets;       /* [E+1]   pool segment starts, 128-aligned          */
     int32_t* slot_map;      /* [T*k]   pool row of route t*k+j, -1 if inactive   */
     int32_t* src;           /* [P]     route t*k+j held by a pool row, -1 = pad  */
-    uint8_t* l1_acts;       /* [P, H]  pool of FP8 rows (written only when the
-                               config sets keep_pool)                            */
-    float* l1_acts_sf;      /* [H/128, P] their scales (pool-row minor; keep_pool) */
-    float* l1_topk_weights; /* [P]     their top-k weights (keep_pool)           */
+    uint8_t* l1_acts;       /* [P, H]  pool of FP8 rows (allocated and written
+                               only when the config sets keep_pool, else NULL)   */
+    float* l1_acts_sf;      /* [H/128, P] their scales (pool-row minor; keep_pool,
+                               else NULL)                                        */
+    float* l1_topk_weights; /* [P]     their top-k weights (keep_pool, else NULL) */
     uint8_t* l2_acts;       /* [P, I]  re-quantised SwiGLU output                */
     float* l2_acts_sf;      /* [I/64, P] its per-64 scales (pool-row minor)      */
     uint16_t* combine_buf;  /* [T*k, H] BF16 L2 partial of each active route     */

@@ -108,14 +108,38 @@ def test_unbuilt_options_are_unsupported(kw):
 
 
 def test_workspace_bytes_cover_the_layer_buffers():
-    cfg = _cfg(max_tokens=8192)
-    n = B.mega_moe_workspace_bytes(cfg)
     R = 8192 * 8
-    P = R + 127 * 32
-    # pool + re-quantised acts + BF16 partials dominate
-    assert n >= P * 7168 + P * 2048 + R * 7168 * 2
-    assert n < 1.1 * (P * 7168 + P * 2048 + R * 7168 * 2) + (64 << 20)
+    P = (R + 127 * 32 + 127) // 128 * 128
+    # re-quantised acts + BF16 partials dominate; the pool copy only with keep_pool
+    n = B.mega_moe_workspace_bytes(_cfg(max_tokens=8192))
+    assert n >= P * 2048 + R * 7168 * 2
+    assert n < 1.1 * (P * 2048 + R * 7168 * 2) + (64 << 20)
+    kept = B.mega_moe_workspace_bytes(_cfg(max_tokens=8192, keep_pool=1))
+    assert kept - n >= P * 7168 + P * (7168 // 128) * 4 + P * 4
+    assert kept - n < P * 7168 + P * (7168 // 128) * 4 + P * 4 + 1024
     assert B.mega_moe_workspace_bytes(_cfg(max_tokens=0)) > 0
+
+
+@pytest.mark.parametrize("n_xcd,cus,seen", [(8, 256, 0), (8, 256, 0xFF), (1, 32, 0), (1, 32, 0x8),
+                                            (2, 64, 0x6), (4, 128, 0xF0)])
+def test_xcd_layout_accepted(n_xcd, cus, seen):
+    # one work queue per XCD: any ids that fall into distinct queues id % n
+    assert B.mega_moe_check_xcd_layout(n_xcd, cus, seen) == 0
+
+
+@pytest.mark.parametrize("n_xcd,cus,seen", [
+    (0, 256, 0), (17, 272, 0), (8, 260, 0), (3, 256, 0),    # count unknown or CUs uneven
+    (8, 256, 0x7F),                                           # an XCD reports no workgroup
+    (2, 64, 0x5),                                             # ids 0 and 2 share queue 0
+    (1, 32, 0x3),                                             # two XCDs behind one count
+])
+def test_xcd_layout_refused(n_xcd, cus, seen):
+    # a layout where an L2 tile could run on another XCD than the L1 tiles it
+    # reads would need cache write-backs the kernel does not do: refused
+    with pytest.raises(B.MegaMoEError) as ei:
+        B.mega_moe_check_xcd_layout(n_xcd, cus, seen)
+    assert ei.value.code == B.MEGA_MOE_ERR_UNSUPPORTED
+    assert "XCD" in B.mega_moe_last_error()
 
 
 def test_forward_rejects_bad_calls_without_touching_the_gpu():

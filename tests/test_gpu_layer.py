@@ -295,6 +295,47 @@ def test_split_phases_match_fused(name, l2_cus):
             assert np.array_equal(a, b), (name, mx, l2_cus)
 
 
+@pytest.mark.parametrize("name", ["ragged", "many_blocks", "skewed"])
+@pytest.mark.parametrize("l2_cus", [4, 12])
+def test_split_phases_match_oracle(name, l2_cus):
+    # the split phases against the oracle itself, not only against the fused
+    # kernel ("PR357 Green-Context Split MegaMoE code review" 5.2: K2 consumes
+    # the L1 output block by block)
+    inp, ref = _case(name)
+    run = G.Runner(inp, split_l2_cus=l2_cus)
+    try:
+        assert run.forward() == 0
+        err = _compare_all(inp, ref, run, f"{name} split_l2_cus {l2_cus}")
+        print(f"{name} split_l2_cus {l2_cus}: y rel frobenius {err:.2e}")
+    finally:
+        run.close()
+
+
+@pytest.mark.parametrize("fast_math", [0, 1])
+def test_subnormal_topk_weights_match_oracle(fast_math):
+    # top-k weights in float32's subnormal range (an underflowed softmax): the
+    # re-quantisation scales amax / 448 are then subnormal (1e-40, 1e-42) or
+    # round to zero (1e-45); codes and scales must still follow the oracle
+    wl = dataclasses.replace(SMALL["ragged"], name="ragged_subnormal")
+    inp = S.make_inputs(wl)
+    tw = inp["topk_weights"]
+    tw[0, 1] = np.float32(1e-40)
+    tw[5, 0] = np.float32(1e-42)
+    tw[9, 2] = np.float32(1e-45)
+    tw[17, 1] = np.float32(3e-38)
+    ref = moe.forward(inp)
+    assert np.any((ref["l2_acts_sf"] > 0) & (ref["l2_acts_sf"] < np.float32(2.0 ** -126)))
+    run = G.Runner(inp, fast_math=fast_math)
+    try:
+        assert run.forward() == 0
+        # (a reciprocal overflowing on these rows would put codes many steps
+        # off, which the one-step rule of the comparison rejects)
+        err = _compare_all(inp, ref, run, f"subnormal weights fast_math {fast_math}")
+        print(f"subnormal top-k weights fast_math {fast_math}: y rel frobenius {err:.2e}")
+    finally:
+        run.close()
+
+
 def test_split_phases_reject_too_many_l2_cus():
     inp, _ = _case("tiny")
     with pytest.raises(B.MegaMoEError) as ei:

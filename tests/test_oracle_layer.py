@@ -86,9 +86,11 @@ def brute_layer(inp, clamp=None):
                 sf = exact.to_f32_value(amax / 448)
                 sfs.append(sf)
                 for v in hs:
+                    # a zero scale (amax = 0, or amax / 448 below the smallest
+                    # float32) gives the code +0 for every value of the group
                     q = v / sf if sf != 0 else Fraction(0)
                     codes.append(exact.e4m3_code_of_value(exact.to_e4m3_value(q),
-                                                          negative_zero=(v < 0)))
+                                                          negative_zero=(v < 0 and sf != 0)))
             ci = [exact.e4m3_int9(c) for c in codes]
             w2i = [[exact.e4m3_int9(int(c)) for c in row] for row in w2[e]]
             part = []
@@ -152,6 +154,31 @@ def test_layer_with_activation_clamp_matches_exact_brute_force():
         s = out["slot_map"][t, j]
         assert list(out["l2_acts"][s]) == r["codes"]
         assert [Fraction(float(v)) for v in out["l2_acts_sf"][:, s]] == r["sf"]
+    yf = codecs.bf16_to_f32(out["y"])
+    for t in range(3):
+        assert [Fraction(float(v)) for v in yf[t]] == y[t]
+
+
+@pytest.mark.slow
+def test_layer_with_subnormal_topk_weights_matches_exact_brute_force():
+    """Top-k weights in float32's subnormal range (an underflowed softmax):
+    1e-40 gives scales amax / 448 that are themselves subnormal, 1e-45 (the
+    smallest subnormal) scales that round to zero.  The float64 oracle must
+    still agree bit for bit with the exact layer."""
+    wl = S.custom(tokens=3, hidden=128, intermediate=128, experts=2, topk=2, seed=31,
+                  weight_seed=32, weight_std=0.05)
+    inp = S.make_inputs(wl)
+    inp["topk_weights"][0, 1] = np.float32(1e-40)
+    inp["topk_weights"][2, 0] = np.float32(1e-45)
+    out = moe.forward(inp)
+    routes, y = brute_layer(inp)
+    s01 = out["l2_acts_sf"][:, out["slot_map"][0, 1]]
+    assert np.all((s01 > 0) & (s01 < np.float32(2.0 ** -126)))     # subnormal scales
+    assert np.all(out["l2_acts_sf"][:, out["slot_map"][2, 0]] == 0)  # scales round to zero
+    for (t, j), r in routes.items():
+        s = out["slot_map"][t, j]
+        assert list(out["l2_acts"][s]) == r["codes"], (t, j)
+        assert [Fraction(float(v)) for v in out["l2_acts_sf"][:, s]] == r["sf"], (t, j)
     yf = codecs.bf16_to_f32(out["y"])
     for t in range(3):
         assert [Fraction(float(v)) for v in yf[t]] == y[t]
