@@ -361,7 +361,7 @@ struct Cfg {
     static constexpr int OFF_DUMMY = OFF_WSB + (WSC_BLOCK ? 2 * BN * 16 : 0);  // 16 bytes per wave
     static constexpr int OFF_TILE = OFF_DUMMY + (WSC_BLOCK ? 64 * NW / 4 : 0);  // per-tile area
     static constexpr int HS = BN / 2 + 4;                 // L1 epilogue h row stride (floats)
-    static constexpr int LDS_BYTES = OFF_TILE + MAX_W_SF * NSB * 4 + BM * 4 + 16 + BM * 4;
+    static constexpr int LDS_BYTES = OFF_TILE + MAX_W_SF * NSB * 4 + BM * 4 + 16 + 2 * BM * 4;
     static_assert((A_BLK + B_BLK) % NW == 0 && A_BLK % NW == 0, "row blocks per wave");
     static_assert(!MX || BN == 128, "MXFP4 weights use 128-column tiles");
     static_assert(WAIT < 64, "vmcnt range");
@@ -379,8 +379,11 @@ struct Lds {
     // weight scales of the tile (FP8 weights): [NSB][KB]
     __device__ float* w_sf() const { return reinterpret_cast<float*>(base + C::OFF_TILE); }
     __device__ float* row_w() const { return w_sf() + MAX_W_SF * C::NSB; }   // top-k weight per row (L1)
-    // [0] the dequeued tile, [2..3] scratch, [4, 4 + BM) the L1 tile's x rows
+    // [0] the dequeued tile, [2..3] scratch, [4, 4 + BM) the L1 tile's x rows,
+    // [4 + BM, 4 + 2 BM) each row's top-k weight exponent offset (row_w holds
+    // w * 2^TINY_W_SHIFT for the rows where it is set)
     __device__ int* tile() const { return reinterpret_cast<int*>(row_w() + C::BM); }
+    __device__ int* row_tiny() const { return tile() + 4 + C::BM; }
 };
 
 // Issues the direct loads of one step.  Wave w fills the 1 KB blocks
@@ -581,9 +584,16 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
     // src[row0 + r] = t*k + j, which reads row t of x and x_sf and takes the
     // top-k weight topk_w[t*k + j]; padding rows point one row past the end
     // of x, where the buffer loads return zeros
+    // A top-k weight below 2^-60 (an underflowed softmax) is kept as
+    // w * 2^64: h = silu(g) * u * w would otherwise fall below float32's
+    // normal range and lose the bits its codes need; the factor comes back
+    // out of the row's scales, exactly, in the quantisation below.
     for (int r = threadIdx.x; r < BM; r += NT) {
         const int f = r < valid ? a.src[row0 + r] : -1;
-        lds.row_w()[r] = f >= 0 ? a.topk_w[f] : 0.0f;
+        const float wt = f >= 0 ? a.topk_w[f] : 0.0f;
+        const bool tiny = fabsf(wt) < 0x1p-60f;
+        lds.row_w()[r] = tiny ? wt * 0x1p64f : wt;
+        lds.row_tiny()[r] = tiny ? 1 : 0;
         lds.tile()[4 + r] = f >= 0 ? f / a.k : a.T;
     }
     __syncthreads();
@@ -807,15 +817,25 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
         for (int q = 0; q < 16; ++q) m = fmaxf(m, fabsf(hv[q]));
         m = fmaxf(m, dpp_move<0xB1>(m));                                // quad_perm [1,0,3,2]
         m = fmaxf(m, dpp_move<0x4E>(m));                                // quad_perm [2,3,0,1]
-        const float sf = m / 448.0f;
-        // h * (1 / sf); below 2^-100 (a row whose top-k weight underflowed,
-        // say) h and sf are first scaled by 2^100, exactly, so that the
-        // reciprocal stays finite; sf = 0 (amax = 0, or amax / 448 below the
-        // smallest float) gives codes of zero
-        const float up = sf < 0x1p-100f ? 0x1p100f : 1.0f;
-        const float inv = sf > 0.0f ? __builtin_amdgcn_rcpf(sf * up) : 0.0f;
+        // codes = h / sf as (h * hsc) * (1 / (sf * ssc)), hsc and ssc powers
+        // of two that keep the reciprocal finite and exact in range.  A row
+        // whose h carries 2^64 (tiny top-k weight): sf = (amax / 448) * 2^-64
+        // rounded once to float32 (via float64), and h / sf = h' / (sf *
+        // 2^64).  Otherwise sf = amax / 448 in float32; below 2^-100 (tiny
+        // SwiGLU outputs) h and sf are scaled by 2^100 first.  sf = 0 (amax
+        // = 0, or amax / 448 below the smallest float) gives codes of zero.
+        float sf, hsc, ssc;
+        if (lds.row_tiny()[r]) {
+            sf = (float)((double)m / 448.0 * 0x1p-64);
+            hsc = 1.0f;
+            ssc = 0x1p64f;
+        } else {
+            sf = m / 448.0f;
+            hsc = ssc = sf < 0x1p-100f ? 0x1p100f : 1.0f;
+        }
+        const float inv = sf > 0.0f ? __builtin_amdgcn_rcpf(sf * ssc) : 0.0f;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) hv[q] *= up;
+        for (int q = 0; q < 16; ++q) hv[q] *= hsc;
         uint32_t code[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
