@@ -31,7 +31,7 @@ EXPORTS = ["mega_moe_create", "mega_moe_forward", "mega_moe_forward_mxfp4", "meg
            "mega_moe_last_error", "mega_moe_workspace_bytes", "mega_moe_token_alignment",
            "mega_moe_plan", "mega_moe_tile_order", "mega_moe_get_views", "mega_moe_set_recv_stats",
            "mega_moe_transform_w1", "mega_moe_profile_begin",
-           "mega_moe_profile_end", "mega_moe_check_xcd_layout"]
+           "mega_moe_profile_end", "mega_moe_check_xcd_layout", "mega_moe_forward_noalloc"]
 
 
 class mega_moe_config(ctypes.Structure):
@@ -106,6 +106,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mega_moe_profile_end.restype = ctypes.c_int
     lib.mega_moe_check_xcd_layout.argtypes = [i32, i32, ctypes.c_uint32]
     lib.mega_moe_check_xcd_layout.restype = ctypes.c_int
+    lib.mega_moe_forward_noalloc.argtypes = [ctypes.POINTER(mega_moe_config), i32] + [vp] * 10 + [vp]
+    lib.mega_moe_forward_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -154,6 +156,16 @@ def mega_moe_forward_mxfp4(handle, num_tokens, x, x_sf, topk_idx, topk_weights, 
     return _check(load().mega_moe_forward_mxfp4(
         handle, num_tokens, ptr(x), ptr(x_sf), ptr(topk_idx), ptr(topk_weights), ptr(w1),
         ptr(w1_scale), ptr(w2), ptr(w2_scale), ptr(y), stream))
+
+
+def mega_moe_forward_noalloc(cfg: mega_moe_config, num_tokens, x, x_sf, topk_idx, topk_weights,
+                             w1, w1_sf, w2, w2_sf, y, dev_errors, stream) -> int:
+    """The allocation-free forward (no handle).  Tensor arguments are device
+    pointers (int) or tensors with data_ptr(); dev_errors may be None."""
+    ptr = lambda t: t if t is None or isinstance(t, int) else t.data_ptr()   # noqa: E731
+    return _check(load().mega_moe_forward_noalloc(
+        ctypes.byref(cfg), num_tokens, ptr(x), ptr(x_sf), ptr(topk_idx), ptr(topk_weights),
+        ptr(w1), ptr(w1_sf), ptr(w2), ptr(w2_sf), ptr(y), ptr(dev_errors), stream))
 
 
 def mega_moe_destroy(handle) -> int:

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -19,6 +20,7 @@ void launch_dispatch(const MoeArgs& a, int gather_blocks, hipStream_t stream);
 int launch_expert_ffn(const MoeArgs& a, int num_cus, hipStream_t stream);
 void launch_combine(const MoeArgs& a, hipStream_t stream);
 hipError_t probe_xcds(uint32_t* word, int num_cus, uint32_t* seen);
+void launch_clear_words(uint32_t* p, int n, hipStream_t stream);
 void launch_transform_w1(const uint8_t* w1, const float* sf, uint8_t* out, float* out_sf, int E,
                          int N, int H, hipStream_t stream);
 }  // namespace mega_moe
@@ -176,6 +178,39 @@ void plan(const mega_moe_config& c, int32_t T, mega_moe_plan_info* p) {
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// The argument block's sizes and options for cfg and its workspace pointers
+// for layout L placed at w.
+void bind_workspace(MoeArgs& a, const mega_moe_config& cfg, const Layout& L, uint8_t* w,
+                    int n_xcd) {
+    std::memset(&a, 0, sizeof a);
+    a.H = cfg.hidden;
+    a.I = cfg.intermediate;
+    a.E = cfg.num_experts;
+    a.k = cfg.num_topk;
+    a.P_cap = L.P_cap;
+    a.wait_spin_limit = 1u << 20;
+    a.act_clamp = cfg.activation_clamp;
+    a.fast_math = cfg.fast_math;
+    a.n_xcd = n_xcd;
+    a.counts = (int32_t*)(w + L.off[L_COUNTS]);
+    a.offsets = (int32_t*)(w + L.off[L_OFFSETS]);
+    a.mb_start = (int32_t*)(w + L.off[L_MBSTART]);
+    a.pb_expert = (int32_t*)(w + L.off[L_PBEXP]);
+    a.slot_map = (int32_t*)(w + L.off[L_SLOTMAP]);
+    a.src = (int32_t*)(w + L.off[L_SRC]);
+    a.chunk_hist = (int32_t*)(w + L.off[L_CHIST]);
+    a.chunk_base = (int32_t*)(w + L.off[L_CBASE]);
+    a.l1_acts = w + L.off[L_L1ACTS];
+    a.l1_sf = (float*)(w + L.off[L_L1SF]);
+    a.l1_w = (float*)(w + L.off[L_L1W]);
+    a.l2_acts = w + L.off[L_L2ACTS];
+    a.l2_sf = (float*)(w + L.off[L_L2SF]);
+    a.comb = (uint16_t*)(w + L.off[L_COMB]);
+    a.ready = (uint32_t*)(w + L.off[L_READY]);
+    a.xcd_info = (int32_t*)(w + L.off[L_XCDINFO]);
+    a.ctrl = (MoeCtrl*)(w + L.off[L_CTRL]);
+}
 
 // XCDs (accelerator dies, each with its own L2) of device dev.  The expert
 // kernel keeps one work queue per XCD so that the L1 tiles of a pool block
@@ -397,36 +432,7 @@ int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out) {
         delete h;
         return fail(rc, "%s", msg.c_str());
     }
-    MoeArgs& a = h->base;
-    std::memset(&a, 0, sizeof a);
-    const Layout& L = h->L;
-    a.H = cfg->hidden;
-    a.I = cfg->intermediate;
-    a.E = cfg->num_experts;
-    a.k = cfg->num_topk;
-    a.P_cap = L.P_cap;
-    a.wait_spin_limit = 1u << 20;
-    a.act_clamp = cfg->activation_clamp;
-    a.fast_math = cfg->fast_math;
-    a.n_xcd = h->n_xcd;
-    uint8_t* w = h->ws;
-    a.counts = (int32_t*)(w + L.off[L_COUNTS]);
-    a.offsets = (int32_t*)(w + L.off[L_OFFSETS]);
-    a.mb_start = (int32_t*)(w + L.off[L_MBSTART]);
-    a.pb_expert = (int32_t*)(w + L.off[L_PBEXP]);
-    a.slot_map = (int32_t*)(w + L.off[L_SLOTMAP]);
-    a.src = (int32_t*)(w + L.off[L_SRC]);
-    a.chunk_hist = (int32_t*)(w + L.off[L_CHIST]);
-    a.chunk_base = (int32_t*)(w + L.off[L_CBASE]);
-    a.l1_acts = w + L.off[L_L1ACTS];
-    a.l1_sf = (float*)(w + L.off[L_L1SF]);
-    a.l1_w = (float*)(w + L.off[L_L1W]);
-    a.l2_acts = w + L.off[L_L2ACTS];
-    a.l2_sf = (float*)(w + L.off[L_L2SF]);
-    a.comb = (uint16_t*)(w + L.off[L_COMB]);
-    a.ready = (uint32_t*)(w + L.off[L_READY]);
-    a.xcd_info = (int32_t*)(w + L.off[L_XCDINFO]);
-    a.ctrl = (MoeCtrl*)(w + L.off[L_CTRL]);
+    bind_workspace(h->base, *cfg, h->L, h->ws, h->n_xcd);
     h->last_T = 0;
     if (cfg->split_l2_cus > 0) {
         rc = split_setup(h, cfg->split_l2_cus);
@@ -463,15 +469,9 @@ struct WeightArgs {
 };
 constexpr int W_FP8_ARGS = 0, W_MXFP4_ARGS = 1;
 
-static int forward_impl(mega_moe_handle* h, int32_t T, const uint8_t* x, const float* x_sf,
-                        const int32_t* topk_idx, const float* topk_weights, const WeightArgs& w,
-                        uint16_t* y, void* stream_v) {
-    if (!h) return fail(MEGA_MOE_ERR_INVALID_ARG, "handle is NULL");
-    if (T < 0 || T > h->cfg.max_tokens)
-        return fail(MEGA_MOE_ERR_INVALID_ARG, "num_tokens %d outside [0, max_tokens=%d]", T,
-                    h->cfg.max_tokens);
-    h->last_T = T;
-    if (T == 0) return ok();
+// Pointer checks of a forward call (T > 0).
+static int check_tensors(const uint8_t* x, const float* x_sf, const int32_t* topk_idx,
+                         const float* topk_weights, const WeightArgs& w, const uint16_t* y) {
     const bool mx = w.fmt == W_MXFP4_ARGS;
     const void* wsc1 = mx ? (const void*)w.w1_e8 : (const void*)w.w1_sf;
     const void* wsc2 = mx ? (const void*)w.w2_e8 : (const void*)w.w2_sf;
@@ -482,18 +482,24 @@ static int forward_impl(mega_moe_handle* h, int32_t T, const uint8_t* x, const f
     if (!aligned(x_sf, 4) || !aligned(topk_idx, 4) || !aligned(topk_weights, 4) ||
         !aligned(wsc1, 4) || !aligned(wsc2, 4))
         return fail(MEGA_MOE_ERR_INVALID_ARG, "scale, index and weight arrays must be 4-byte aligned");
-    hipStream_t stream = (hipStream_t)stream_v;
+    return MEGA_MOE_OK;
+}
+
+// The argument block of one call: the plan for T tokens and the tensors.
+static void call_args(MoeArgs& a, const mega_moe_config& cfg, int32_t T, const uint8_t* x,
+                      const float* x_sf, const int32_t* topk_idx, const float* topk_weights,
+                      const WeightArgs& w, uint16_t* y) {
+    const bool mx = w.fmt == W_MXFP4_ARGS;
     mega_moe_plan_info p;
-    plan(h->cfg, T, &p);
+    plan(cfg, T, &p);
     if (mx) {
         // MXFP4 weights run on 128-column tiles only
         p.block_n = 128;
-        p.l1_n_blocks = 2 * h->cfg.intermediate / 128;
-        p.l2_n_blocks = h->cfg.hidden / 128;
+        p.l1_n_blocks = 2 * cfg.intermediate / 128;
+        p.l2_n_blocks = cfg.hidden / 128;
     }
-    MoeArgs a = h->base;
     a.T = T;
-    a.R = T * h->cfg.num_topk;
+    a.R = T * cfg.num_topk;
     a.block_m = p.block_m;
     a.block_n = p.block_n;
     a.nb1 = p.l1_n_blocks;
@@ -513,6 +519,22 @@ static int forward_impl(mega_moe_handle* h, int32_t T, const uint8_t* x, const f
     a.w2_sf = w.w2_sf;
     a.w2_e8 = w.w2_e8;
     a.y = y;
+}
+
+static int forward_impl(mega_moe_handle* h, int32_t T, const uint8_t* x, const float* x_sf,
+                        const int32_t* topk_idx, const float* topk_weights, const WeightArgs& w,
+                        uint16_t* y, void* stream_v) {
+    if (!h) return fail(MEGA_MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (T < 0 || T > h->cfg.max_tokens)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "num_tokens %d outside [0, max_tokens=%d]", T,
+                    h->cfg.max_tokens);
+    h->last_T = T;
+    if (T == 0) return ok();
+    int rc = check_tensors(x, x_sf, topk_idx, topk_weights, w, y);
+    if (rc) return rc;
+    hipStream_t stream = (hipStream_t)stream_v;
+    MoeArgs a = h->base;
+    call_args(a, h->cfg, T, x, x_sf, topk_idx, topk_weights, w, y);
     const int gather_blocks = h->cfg.keep_pool ? (a.R < 16384 ? a.R : 16384) : 0;
     const int call = h->prof_used < h->prof_max ? h->prof_used++ : -1;
     if (call >= 0) hipEventRecord(prof_event(h, call, 0), stream);
@@ -655,6 +677,137 @@ int mega_moe_get_views(mega_moe_handle* h, mega_moe_views* v) {
     v->combine_buf = a.comb;
     v->pool_rows_capacity = a.P_cap;
     v->last_num_tokens = h->last_T;
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward.  Its workspace is the file-scope device array
+// `scratch` below: every GPU the library runs on holds its own copy of it
+// until the process ends.  Host code never uses the array's name as an
+// address (in host code it is only a stand-in for the symbol): the set-up
+// of each device asks the runtime for that device's address of it, once,
+// with the device current, and every kernel argument is derived from that.
+// The control record (queue heads, error bits) sits at its start, the
+// per-call layout after it.
+// ---------------------------------------------------------------------------
+constexpr int64_t NOALLOC_CTRL_BYTES = 256;
+static_assert(sizeof(MoeCtrl) <= NOALLOC_CTRL_BYTES, "control record");
+
+int mega_moe_forward_noalloc(const mega_moe_config* cfg, int32_t T, const uint8_t* x,
+                             const float* x_sf, const int32_t* topk_idx,
+                             const float* topk_weights, const uint8_t* w1, const float* w1_sf,
+                             const uint8_t* w2, const float* w2_sf, uint16_t* y,
+                             uint32_t* dev_errors, void* stream_v);
+
+}  // extern "C"
+
+static __device__ __align__(256) uint8_t scratch[MEGA_MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+
+struct NoallocDevice {
+    std::once_flag once;
+    int rc = MEGA_MOE_OK;
+    std::string err;
+    uint8_t* ptr = nullptr;       // this device's address of `scratch`
+    int num_cus = 0, n_xcd = 0;
+    std::mutex clear_mu;
+    bool cleared = false;         // the control record's first clear was issued
+};
+
+NoallocDevice g_noalloc[NOALLOC_MAX_DEVICES];
+
+// One-time set-up of device dev (current on the calling thread): the device
+// checks of mega_moe_create (without its probe kernel, which would
+// synchronise) and the device address of `scratch`.
+void noalloc_setup(NoallocDevice& d, int dev) {
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) {
+        d.rc = fail(MEGA_MOE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    } else if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+        d.rc = fail(MEGA_MOE_ERR_UNSUPPORTED, "device %d is %s, this library is built for gfx950",
+                    dev, prop.gcnArchName);
+    } else if ((d.rc = xcd_count(dev, prop.multiProcessorCount, &d.n_xcd)) == MEGA_MOE_OK) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            d.rc = fail(MEGA_MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        } else {
+            d.ptr = static_cast<uint8_t*>(p);
+            d.num_cus = prop.multiProcessorCount;
+        }
+    }
+    if (d.rc) d.err = g_last_error;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mega_moe_forward_noalloc(const mega_moe_config* cfg, int32_t T, const uint8_t* x,
+                             const float* x_sf, const int32_t* topk_idx,
+                             const float* topk_weights, const uint8_t* w1, const float* w1_sf,
+                             const uint8_t* w2, const float* w2_sf, uint16_t* y,
+                             uint32_t* dev_errors, void* stream_v) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (cfg->keep_pool || cfg->split_l2_cus)
+        return fail(MEGA_MOE_ERR_INVALID_ARG,
+                    "the allocation-free forward takes neither keep_pool nor split_l2_cus");
+    if (T < 0 || T > cfg->max_tokens)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "num_tokens %d outside [0, max_tokens=%d]", T,
+                    cfg->max_tokens);
+    if (T == 0) return ok();
+    const WeightArgs w{W_FP8_ARGS, w1, w1_sf, nullptr, w2, w2_sf, nullptr};
+    rc = check_tensors(x, x_sf, topk_idx, topk_weights, w, y);
+    if (rc) return rc;
+    if (dev_errors && !aligned(dev_errors, 4))
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "dev_errors must be 4-byte aligned");
+    // the layout of this call: the workspace of a handle sized for T tokens
+    mega_moe_config c = *cfg;
+    c.max_tokens = T;
+    const Layout L = make_layout(c);
+    const int64_t need = NOALLOC_CTRL_BYTES + L.total;
+    if (need > (int64_t)MEGA_MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MEGA_MOE_ERR_INVALID_ARG,
+                    "%d tokens need %lld bytes of scratch; the allocation-free forward has %lld "
+                    "(use a handle from mega_moe_create for larger batches)", T, (long long)need,
+                    (long long)MEGA_MOE_NOALLOC_SCRATCH_BYTES);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MEGA_MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+        return fail(MEGA_MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev,
+                    NOALLOC_MAX_DEVICES);
+    NoallocDevice& d = g_noalloc[dev];
+    std::call_once(d.once, noalloc_setup, std::ref(d), dev);
+    if (d.rc) return fail(d.rc, "%s", d.err.c_str());
+    hipStream_t stream = (hipStream_t)stream_v;
+    {
+        // the control record starts cleared (device globals are zero-filled
+        // when the code object loads; this first clear does not rely on it)
+        std::lock_guard<std::mutex> lk(d.clear_mu);
+        if (!d.cleared) {
+            launch_clear_words(reinterpret_cast<uint32_t*>(d.ptr),
+                               (int)(NOALLOC_CTRL_BYTES / 4), stream);
+            d.cleared = true;
+        }
+    }
+    MoeArgs a;
+    bind_workspace(a, c, L, d.ptr + NOALLOC_CTRL_BYTES, d.n_xcd);
+    a.ctrl = reinterpret_cast<MoeCtrl*>(d.ptr);
+    a.err_move = 1;
+    a.err_out = dev_errors;
+    call_args(a, c, T, x, x_sf, topk_idx, topk_weights, w, y);
+    launch_dispatch(a, 0, stream);
+    launch_expert_ffn(a, d.num_cus, stream);
+    launch_combine(a, stream);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(MEGA_MOE_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -28,6 +28,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __global__ void __launch_bounds__(COMBINE_THREADS)
 moe_combine(MoeArgs a) {
+    if (a.err_move && blockIdx.x == 0 && threadIdx.x == 0) {
+        // every kernel that can raise an error bit of this call ran before
+        // this one on the stream
+        const uint32_t e = __hip_atomic_exchange(&a.ctrl->error, 0u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+        if (e && a.err_out) atomicOr(a.err_out, e);
+    }
     const int col_blocks = (a.H + COMBINE_COLS - 1) / COMBINE_COLS;
     const int t = blockIdx.x / col_blocks;
     const int col = (blockIdx.x - t * col_blocks) * COMBINE_COLS + threadIdx.x * 8;

@@ -327,6 +327,16 @@ moe_dispatch_gather(MoeArgs a) {
     }
 }
 
+__global__ void __launch_bounds__(256) moe_clear_words(uint32_t* p, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+// Clears n words at p with a kernel (not a memory set, so that a captured
+// call records a kernel node).
+void launch_clear_words(uint32_t* p, int n, hipStream_t stream) {
+    hipLaunchKernelGGL(moe_clear_words, dim3(1), dim3(256), 0, stream, p, n);
+}
+
 void launch_dispatch(const MoeArgs& a, int gather_blocks, hipStream_t stream) {
     if (a.num_chunks <= SMALL_CHUNKS) {
         hipLaunchKernelGGL(moe_dispatch_small, dim3(1), dim3(SCAN_THREADS), 0, stream, a);

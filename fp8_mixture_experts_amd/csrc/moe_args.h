@@ -71,6 +71,11 @@ struct MoeArgs {
     int32_t* recv_stats;  // [E] caller-owned cumulative routes per expert, or null
     int32_t* xcd_info;    // [2 * MAX_XCD] first pool block and block count of each XCD
     MoeCtrl* ctrl;
+    // 1: the combine moves the call's device error bits out of ctrl (ORs them
+    // into *err_out when that is set) and clears them, so that every call
+    // reports its own; 0: they stay sticky in ctrl until the host reads them
+    int32_t err_move;
+    uint32_t* err_out;
 };
 
 constexpr int DISPATCH_CHUNK = 1024;    // routes per dispatch workgroup

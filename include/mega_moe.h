@@ -159,6 +159,38 @@ int mega_moe_forward_mxfp4(mega_moe_handle* h, int32_t num_tokens,
                            const uint8_t* w2, const uint8_t* w2_scale,
                            uint16_t* y, void* stream);
 
+/*
+ * mega_moe_forward without a handle, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It calls no hipMalloc, hipFree or other allocating
+ * routine.  Its workspace is a device array inside the library of
+ * MEGA_MOE_NOALLOC_SCRATCH_BYTES (128 MiB), one per GPU, held from the first
+ * use until the process ends.
+ *   cfg         as for mega_moe_create; keep_pool and split_l2_cus must be 0.
+ *               num_tokens <= cfg->max_tokens.
+ *   num_tokens  a call needs mega_moe_workspace_bytes(cfg with max_tokens =
+ *               num_tokens) + 256 bytes of the array; a larger call returns
+ *               MEGA_MOE_ERR_INVALID_ARG (up to 948 tokens of top-8 at hidden 7168,
+ *               intermediate 2048 and 32 experts; a handle has no such limit).
+ *   tensors     as for mega_moe_forward (FP8 weights).
+ *   dev_errors  optional device word (NULL: discarded) into which the call
+ *               ORs its MEGA_MOE_DEVERR_* bits on the stream, after its last
+ *               kernel; each call starts with no bits set.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (two streams, two threads) race and
+ * must be ordered by the caller.  The first call on each device does a
+ * one-time host set-up (device checks and the array's address) and issues one
+ * small clearing kernel on `stream`; later calls launch the same kernels as
+ * mega_moe_forward and nothing else.  Errors as mega_moe_forward.
+ */
+#define MEGA_MOE_NOALLOC_SCRATCH_BYTES (128u << 20)
+int mega_moe_forward_noalloc(const mega_moe_config* cfg, int32_t num_tokens,
+                             const uint8_t* x, const float* x_sf,
+                             const int32_t* topk_idx, const float* topk_weights,
+                             const uint8_t* w1, const float* w1_sf,
+                             const uint8_t* w2, const float* w2_sf,
+                             uint16_t* y, uint32_t* dev_errors, void* stream);
+
 /* Frees the workspace and the handle; NULL is accepted. */
 int mega_moe_destroy(mega_moe_handle* h);
 

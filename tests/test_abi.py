@@ -227,3 +227,24 @@ def test_tile_order_rejects_bad_arguments():
     plan.block_m = 48
     with pytest.raises(B.MegaMoEError):
         B.mega_moe_tile_order(plan, [0, 4], 8, 1)
+
+
+def test_noalloc_forward_refusals_need_no_gpu():
+    # every check of the allocation-free forward runs before it touches a
+    # device: the pointers below are aligned stand-ins that are never used
+    fake = 1 << 20
+    tensors = [fake] * 9
+    big = _cfg(max_tokens=8192)
+    with pytest.raises(B.MegaMoEError) as ei:
+        B.mega_moe_forward_noalloc(big, 8192, *tensors, None, None)
+    assert ei.value.code == B.MEGA_MOE_ERR_INVALID_ARG
+    assert "scratch" in B.mega_moe_last_error()
+    for cfg, n in ((_cfg(max_tokens=128, keep_pool=1), 128),
+                   (_cfg(max_tokens=128, split_l2_cus=4), 128),
+                   (_cfg(max_tokens=128), 129)):
+        with pytest.raises(B.MegaMoEError) as ei:
+            B.mega_moe_forward_noalloc(cfg, n, *tensors, None, None)
+        assert ei.value.code == B.MEGA_MOE_ERR_INVALID_ARG
+    with pytest.raises(B.MegaMoEError):
+        B.mega_moe_forward_noalloc(_cfg(max_tokens=128), 128, *([0] * 9), None, None)
+    assert B.mega_moe_forward_noalloc(_cfg(max_tokens=128), 0, *([0] * 9), None, None) == 0
