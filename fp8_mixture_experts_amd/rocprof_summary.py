@@ -3,9 +3,18 @@
 
     python -m fp8_mixture_experts_amd.rocprof_summary trace DB OUT "COMMAND"
     python -m fp8_mixture_experts_amd.rocprof_summary traffic FETCH_DB WRITE_DB OUT WORKLOAD "COMMAND" COPY_BYTES
+    python -m fp8_mixture_experts_amd.rocprof_summary mfma DB OUT WORKLOAD "COMMAND" FLOPS [CUS XCDS]
 
 ``trace`` reads a ``--kernel-trace --stats`` database and writes one line per
 kernel (calls, average and total duration, launch shape, registers, LDS).
+
+``mfma`` reads one ``--pmc --kernel-trace`` database of the matrix-core
+counters (``SQ_INSTS_VALU_MFMA_MOPS_F16`` / ``_F8`` in units of 512 FLOPs,
+``SQ_VALU_MFMA_BUSY_CYCLES``, ``GRBM_GUI_ACTIVE`` ...) and writes the expert
+kernel's per-launch averages with what follows from them: FLOPs per matrix
+type (checked against the algorithmic FLOPS), the shader clock (GUI-active
+cycles per XCD over the traced duration), the matrix-core busy fraction of
+the SIMD cycles, and the achieved rate against the FP8 peak.
 
 ``traffic`` reads two ``--pmc`` databases of the same bench command, one with
 ``FETCH_SIZE`` and one with ``WRITE_SIZE`` (KiB per dispatch), taken with
@@ -152,6 +161,64 @@ def traffic(fetch_db, write_db, out, workload, command, copy_bytes):
     return text
 
 
+def _durations(con):
+    """Mean traced duration (ns) per kernel name, if the run traced kernels."""
+    for q in ('select name, avg("end" - start) from kernels group by name',
+              "select name, avg(duration) from kernels group by name",
+              "select name, average * 1000.0 from top_kernels"):
+        try:
+            return {n: float(d) for n, d in con.execute(q)}
+        except sqlite3.Error:
+            continue
+    return {}
+
+
+def mfma(db, out, workload, command, flops, cus=256, xcds=8):
+    con = _db(db)
+    counters = [r[0] for r in con.execute("select distinct counter_name from counters_collection")]
+    vals = {}
+    kname = None
+    for c in sorted(counters):
+        name, (v, n) = _pick(_counter(con, c), (EXPERT_KERNEL,), "expert")
+        kname = name
+        vals[c] = (v, n)
+    dur = _durations(con)
+    dur_ns = next((d for n, d in dur.items() if n == kname), None)
+    lines = [f"# matrix-core counters of {kname} on the {workload} workload "
+             "(rocprofv3 --pmc --kernel-trace, averages per launch)",
+             f"# command: {command}"]
+    for c in sorted(vals):
+        lines.append(f"{c}: {vals[c][0]:.6g}   (dispatches: {vals[c][1]})")
+    simds = 4 * cus
+    mops16 = vals.get("SQ_INSTS_VALU_MFMA_MOPS_F16", (0.0, 0))[0]
+    mops8 = vals.get("SQ_INSTS_VALU_MFMA_MOPS_F8", (0.0, 0))[0]
+    mfma_flops = 512.0 * (mops16 + mops8)
+    lines += [f"f16_mfma_flops: {512.0 * mops16:.6g}",
+              f"f8_mfma_flops: {512.0 * mops8:.6g}",
+              f"algorithmic_flops: {flops:.6g}",
+              f"mfma_flops_over_algorithmic: {mfma_flops / flops:.4f}"]
+    gui = vals.get("GRBM_GUI_ACTIVE", (0.0, 0))[0]
+    busy = vals.get("SQ_VALU_MFMA_BUSY_CYCLES", (0.0, 0))[0]
+    if gui:
+        cycles = gui / xcds
+        lines.append(f"kernel_cycles_per_xcd: {cycles:.6g}")
+        if busy:
+            lines.append(f"mfma_busy_fraction_of_simd_cycles: {busy / (simds * cycles):.4f}")
+        if dur_ns:
+            lines.append(f"traced_duration_us: {dur_ns / 1e3:.2f}")
+            lines.append(f"shader_clock_ghz: {cycles / dur_ns:.3f}")
+    if dur_ns:
+        rate = flops / (dur_ns * 1e-9)
+        lines += [f"achieved_tflops: {rate / 1e12:.1f}",
+                  f"fraction_of_fp8_peak_5000_tflops: {rate / 5e15:.4f}",
+                  f"fraction_of_exact_path_peak_3000_tflops: {rate / 3e15:.4f}"]
+    lines += [f"workload: {workload}", f"sources_sha256: {sources_sha256()}"]
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    return text
+
+
 def read_traffic(path, workload):
     """Calibrated traffic per launch from a summary, or None when it is stale."""
     if not os.path.exists(path):
@@ -169,6 +236,9 @@ def read_traffic(path, workload):
 def main(argv):
     if len(argv) >= 4 and argv[0] == "trace":
         print(trace(argv[1], argv[2], argv[3]), end="")
+    elif len(argv) >= 6 and argv[0] == "mfma":
+        extra = [int(v) for v in argv[6:8]]
+        print(mfma(argv[1], argv[2], argv[3], argv[4], float(argv[5]), *extra), end="")
     elif len(argv) >= 7 and argv[0] == "traffic":
         print(traffic(argv[1], argv[2], argv[3], argv[4], argv[5], int(argv[6])), end="")
     else:
