@@ -505,6 +505,8 @@ static void call_args(MoeArgs& a, const mega_moe_config& cfg, int32_t T, const u
     a.nb1 = p.l1_n_blocks;
     a.nb2 = p.l2_n_blocks;
     a.n_major = p.l2_n_major;
+    // cross-XCD tail balancing pays with the large batches of the N-major schedule
+    a.steal = p.l2_n_major;
     a.xcd_group = xcd_group_for(p.block_m);
     a.num_chunks = (a.R + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK;
     a.x = x;

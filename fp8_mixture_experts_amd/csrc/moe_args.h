@@ -11,9 +11,8 @@ constexpr int MAX_XCD = 16;
 
 // Control record in device memory, reset by the dispatch scan of every call.
 struct MoeCtrl {
-    int32_t next_tile[MAX_XCD];     // work queue head of each XCD's tiles (L1 tiles only
-                                    // when the phases run as two kernels)
-    int32_t next_tile_l2[MAX_XCD];  // each XCD's L2 tile queue when they do
+    int32_t next_tile[MAX_XCD];     // head of each XCD's queue of L1 tiles
+    int32_t next_tile_l2[MAX_XCD];  // head of each XCD's queue of L2 tiles
     int32_t total_mb;               // number of pool blocks (BLOCK_M rows) over all experts
     uint32_t error;                 // sticky MEGA_MOE_DEVERR_* bits
     int32_t pad[2];
@@ -38,6 +37,7 @@ struct MoeArgs {
     int32_t fast_math;  // 1: hardware exp2 and reciprocal in SiLU
     int32_t w_fmt;      // 0: FP8 weights with float block scales, 1: MXFP4 weights
     int32_t phase;      // expert kernel: 0 L1 and L2 tiles, 1 L1 tiles only, 2 L2 tiles only
+    int32_t steal;      // phase 0: workgroups out of tiles take L2 tiles queued on other XCDs
 
     // inputs (caller-owned)
     const uint8_t* x;
@@ -67,7 +67,8 @@ struct MoeArgs {
     uint8_t* l2_acts;     // [P_cap, I]
     float* l2_sf;         // [I/64, P_cap]
     uint16_t* comb;       // [R, H]
-    uint32_t* ready;      // [PB_cap] finished L1 tiles per pool block
+    uint32_t* ready;      // [PB_cap] finished L1 tiles per pool block, plus
+                          // READY_PUBLISHED once the block is written back
     int32_t* recv_stats;  // [E] caller-owned cumulative routes per expert, or null
     int32_t* xcd_info;    // [2 * MAX_XCD] first pool block and block count of each XCD
     MoeCtrl* ctrl;
@@ -77,6 +78,10 @@ struct MoeArgs {
     int32_t err_move;
     uint32_t* err_out;
 };
+
+// ready[pb] bit set when the pool block's L1 output has been written back
+// from its XCD's L2 (readable from every XCD)
+constexpr uint32_t READY_PUBLISHED = 0x80000000u;
 
 constexpr int DISPATCH_CHUNK = 1024;    // routes per dispatch workgroup
 constexpr int DISPATCH_THREADS = 256;

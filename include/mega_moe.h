@@ -73,7 +73,10 @@ typedef struct mega_moe_config {
     int32_t fast_math;        /* 0: expf and IEEE division in SiLU; 1: hardware
                                  exp2 and reciprocal (a few float32 ulps)        */
     int32_t block_m;          /* 0 = automatic (SM90 design 13.1), else 32/64/128 */
-    int32_t l2_n_major;       /* -1 automatic (12.2), 0 M-major, 1 N-major L2 order */
+    int32_t l2_n_major;       /* -1 automatic (12.2), 0 M-major, 1 N-major L2 order;
+                                 the N-major schedule (large batches) also lets
+                                 workgroups whose XCD ran out of tiles take L2
+                                 tiles queued on other XCDs                      */
     int32_t block_n;          /* output columns per expert-kernel tile: 0 = automatic,
                                  128, or 256 (needs 2I % 256 == 0, H % 256 == 0 and
                                  block_m != 32) */

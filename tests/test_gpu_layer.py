@@ -76,6 +76,23 @@ def test_layer_matches_oracle(name, keep_pool):
         run.close()
 
 
+@pytest.mark.parametrize("name", ["one_expert", "tiny", "ragged"])
+def test_tiles_taken_across_xcds_match_oracle(name):
+    # few pool blocks: most XCDs have no tiles of their own and take the L2
+    # tiles queued on the others, reading blocks published through an L2
+    # write-back.  Repeated on fresh handles (reused addresses, caches holding
+    # earlier calls' lines): an ordering fault there shows only now and then.
+    # (the tail balancing runs with the N-major schedule, forced here)
+    inp, ref = _case(name)
+    for rep in range(6):
+        run = G.Runner(inp, l2_n_major=1)
+        try:
+            assert run.forward() == 0
+            _compare_all(inp, ref, run, f"{name} repeat {rep}")
+        finally:
+            run.close()
+
+
 def _biting_clamp(inp):
     """A clamp below about a third of the |gate| and |up| values of expert 0."""
     acc = moe.l1_gemm(inp["x"][:8], inp["x_sf"][:8], inp["w1"][0], inp["w1_sf"][0])

@@ -2,6 +2,11 @@
 
 * No instance spills to scratch, and each fits the 256 registers per lane that
   two workgroups per CU leave every wave.
+* Every L2 write-back (``buffer_wbl2``, the release before a pool block is
+  marked readable from other XCDs) and every L2 invalidation (``buffer_inv``,
+  the acquire of a workgroup reading another XCD's block) is followed by a
+  full wait before the next atomic or barrier: without it the mark can become
+  visible, or the other waves can load, before the cache operation is done.
 * No full drain of the direct global->LDS loads (``s_waitcnt vmcnt(0)``) sits
   in the matrix code.  The K loop keeps S - 1 steps of loads in flight and
   waits only for the oldest; a drain there serialises the pipeline without
@@ -72,3 +77,18 @@ def test_no_load_drain_in_the_matrix_code(kernels):
                 window = body[k + 1:k + 60]
                 assert not any("v_mfma" in x for x in window), (
                     f"{name}: full load drain before matrix code at line {k}")
+
+
+def test_cache_writeback_and_invalidate_are_waited_for(kernels):
+    bodies, _ = kernels
+    seen = 0
+    for name, body in bodies.items():
+        code = [x.strip() for x in body if x.startswith("\t") and not x.strip().startswith(";")]
+        for k, line in enumerate(code):
+            if line.startswith(("buffer_wbl2", "buffer_inv")):
+                seen += 1
+                nxt = [x for x in code[k + 1:k + 40]
+                       if x.startswith(("s_waitcnt", "global_atomic", "buffer_atomic", "s_barrier"))]
+                assert nxt and nxt[0].startswith("s_waitcnt") and "vmcnt(0)" in nxt[0], (
+                    f"{name}: {line} not followed by a full wait: {nxt[:3]}")
+    assert seen >= 8
