@@ -12,7 +12,9 @@ weight-stream rate (bytes of the active experts' FP8 weights and scales per
 step / step time); the prefill workload reports FP8 TFLOP/s instead.  With
 the decode workload the line also carries ``prefill``: the same measurement
 of the 8192-token prefill batch (Zipf(1.2) routing), the compute-bound half
-of the metric, in the same process with the same step counts.
+of the metric, in the same process with the same step counts; it is measured
+first, so that the decode steps run on a GPU already under load (a GPU that
+has been idle needs about 15 ms of work to reach its steady clock).
 
 W untimed warm-up steps, then the K timed steps, twice.  The first pass is
 plain: its wall time, bracketed by device synchronisations, gives
@@ -256,6 +258,16 @@ def main():
     from fp8_mixture_experts_amd import rocprof_summary as RS
 
     name = args.workload
+    pre = None
+    if name == "decode" and not args.no_prefill:
+        # the compute-bound half of the metric: the 8192-token prefill batch,
+        # the same number of warm-up and timed steps.  It runs first, so the
+        # decode steps are then timed on a GPU already under load, as in a
+        # running model: after an idle period the GPU takes about 50 decode
+        # steps (15 ms) to reach its steady clock (measured on MI355X:
+        # 282-306 us per expert kernel over the first 50 steps, 266-267 us
+        # after), which a few warm-up steps alone would time instead.
+        _, _, pre = measure("prefill", args, torch, B, S, RS)
     inp, work, res = measure(name, args, torch, B, S, RS)
     out = {
         "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
@@ -264,10 +276,7 @@ def main():
         "dtype": "fp8_e4m3 x mxfp4" if work["mx"] else "fp8_e4m3", "data": "synthetic",
     }
     out.update({k: v for k, v in res.items() if k not in ("value", "unit", "ms_per_step")})
-    if name == "decode" and not args.no_prefill:
-        # the compute-bound half of the metric: the 8192-token prefill batch,
-        # the same number of warm-up and timed steps
-        _, _, pre = measure("prefill", args, torch, B, S, RS)
+    if pre is not None:
         out["prefill"] = pre
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
