@@ -886,6 +886,23 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
     }
 }
 
+// NB matrix products, each folded into an accumulator with a per-lane scale:
+// acc(i) += scale(i) * prod(i), i = 0 .. NB-1.  Product i + 1 is issued
+// before the adds of product i (two result buffers), so the vector ALU works
+// on one product while the matrix core computes the next; written as plain
+// "product, then its adds", the compiler gives every product the same
+// result registers and the adds wait out each product's whole latency.
+template <int NB, typename Prod, typename Fold>
+__device__ __forceinline__ void prod_fold_pipeline(Prod&& prod, Fold&& fold) {
+    v16f d[2];
+    d[0] = prod(0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        if (i + 1 < NB) d[(i + 1) & 1] = prod(i + 1);
+        fold(i, d[i & 1]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // L2 tile: pool rows [row0, row0 + valid) of expert e, W2 N block nb.
 // ---------------------------------------------------------------------------
@@ -971,41 +988,51 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                     fb[q][0] = fp4_half_raw(stg + C::OFF_B, ly.g0 + q, 0);
                     fb[q][1] = fp4_half_raw(stg + C::OFF_B, ly.g0 + q, 1);
                 }
+                Frag fa[LY::NJ];
+                float sa[LY::NJ][2];
 #pragma unroll
                 for (int j = 0; j < LY::NJ; ++j) {
-                    const int sl = ly.s0 + j;
-                    const Frag fa = read_frag2(stg, sl);
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const float sa = lane_row_scale(sfa + 4 * hh * BM, sl);
-#pragma unroll
-                        for (int q = 0; q < LY::NG; ++q) {
-                            const int e8 = (int)((wsc[q] >> (8 * (2 * hh + g))) & 0xFFu);
-                            const v16f d = mfma_mx(fb[q][hh], fa.h[hh], zero, e8);
-                            acc[j][q] = __builtin_elementwise_fma(d, v16f(sa), acc[j][q]);
-                        }
-                    }
+                    fa[j] = read_frag2(stg, ly.s0 + j);
+                    sa[j][0] = lane_row_scale(sfa, ly.s0 + j);
+                    sa[j][1] = lane_row_scale(sfa + 4 * BM, ly.s0 + j);
                 }
+                // product i: half i / (NJ NG), slice (i / NG) % NJ, group i % NG
+                constexpr int NB = 2 * LY::NJ * LY::NG;
+                prod_fold_pipeline<NB>(
+                    [&](int i) {
+                        const int hh = i / (LY::NJ * LY::NG), j = (i / LY::NG) % LY::NJ, q = i % LY::NG;
+                        const int e8 = (int)((wsc[q] >> (8 * (2 * hh + g))) & 0xFFu);
+                        return mfma_mx(fb[q][hh], fa[j].h[hh], zero, e8);
+                    },
+                    [&](int i, const v16f& d) {
+                        const int hh = i / (LY::NJ * LY::NG), j = (i / LY::NG) % LY::NJ, q = i % LY::NG;
+                        acc[j][q] = __builtin_elementwise_fma(d, v16f(sa[j][hh]), acc[j][q]);
+                    });
                 return;
             }
             const float sw = lds.w_sf()[ly.sblock() * KB + kb];
             Frag fb[LY::NG];
 #pragma unroll
             for (int q = 0; q < LY::NG; ++q) fb[q] = read_frag2(stg + C::OFF_B, ly.g0 + q);
+            Frag fa[LY::NJ];
+            float svw[LY::NJ][2];
 #pragma unroll
             for (int j = 0; j < LY::NJ; ++j) {
-                const int sl = ly.s0 + j;
-                const Frag fa = read_frag2(stg, sl);
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const float svw = lane_row_scale(sfa + 4 * hh * BM, sl) * sw;
-#pragma unroll
-                    for (int q = 0; q < LY::NG; ++q) {
-                        const v16f d = mfma_f8(fb[q].h[hh], fa.h[hh], zero);
-                        acc[j][q] = __builtin_elementwise_fma(d, v16f(svw), acc[j][q]);
-                    }
-                }
+                fa[j] = read_frag2(stg, ly.s0 + j);
+                svw[j][0] = lane_row_scale(sfa, ly.s0 + j) * sw;
+                svw[j][1] = lane_row_scale(sfa + 4 * BM, ly.s0 + j) * sw;
             }
+            // product i: half i / (NJ NG), slice (i / NG) % NJ, group i % NG
+            constexpr int NB = 2 * LY::NJ * LY::NG;
+            prod_fold_pipeline<NB>(
+                [&](int i) {
+                    const int hh = i / (LY::NJ * LY::NG), j = (i / LY::NG) % LY::NJ, q = i % LY::NG;
+                    return mfma_f8(fb[q].h[hh], fa[j].h[hh], zero);
+                },
+                [&](int i, const v16f& d) {
+                    const int hh = i / (LY::NJ * LY::NG), j = (i / LY::NG) % LY::NJ, q = i % LY::NG;
+                    acc[j][q] = __builtin_elementwise_fma(d, v16f(svw[j][hh]), acc[j][q]);
+                });
         });
 
         // ---- epilogue: BF16 partials, staged so each route row is stored whole ----
