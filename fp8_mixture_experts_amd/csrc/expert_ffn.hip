@@ -372,12 +372,16 @@ struct Cfg {
     static constexpr int OFF_DUMMY = OFF_WSB + (WSC_BLOCK ? 2 * BN * 16 : 0);  // 16 bytes per wave
     static constexpr int OFF_TILE = OFF_DUMMY + (WSC_BLOCK ? 64 * NW / 4 : 0);  // per-tile area
     static constexpr int HS = BN / 2 + 4;                 // L1 epilogue h row stride (floats)
+    // L2 epilogue BF16 row stride (elements): 16 bytes past a multiple of the
+    // 256 bytes that span the 64 LDS banks, so the 8-byte writes of one
+    // column group's 32 rows (and the two lane halves) fall on distinct banks
+    static constexpr int YS = BN + 8;
     static constexpr int LDS_BYTES = OFF_TILE + MAX_W_SF * NSB * 4 + BM * 4 + 16 + 2 * BM * 4;
     static_assert((A_BLK + B_BLK) % NW == 0 && A_BLK % NW == 0, "row blocks per wave");
     static_assert(!MX || BN == 128, "MXFP4 weights use 128-column tiles");
     static_assert(WAIT < 64, "vmcnt range");
     static_assert(WPC * LDS_BYTES <= 160 * 1024, "LDS per CU");
-    static_assert(BM * BN * 2 <= S * STAGE && BM * HS * 4 <= S * STAGE, "epilogue buffers");
+    static_assert(BM * YS * 2 <= S * STAGE && BM * HS * 4 <= S * STAGE, "epilogue buffers");
 };
 
 template <int MS, int BNT, int WF = W_FP8>
@@ -959,7 +963,8 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
         I / 32);
 
     const v16f zero = v16f{};
-    uint16_t* stage = reinterpret_cast<uint16_t*>(lds.stage(0));  // BF16 [BM][BN] after the k loop
+    constexpr int YS = C::YS;
+    uint16_t* stage = reinterpret_cast<uint16_t*>(lds.stage(0));  // BF16 [BM][YS] after the k loop
 
     dispatch_act<MS>(act, [&](auto tag) {
         constexpr int ACT = decltype(tag)::value;
@@ -1049,7 +1054,7 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                     const uint2 w2{(uint32_t)bf16_rne(r[4 * t]) | ((uint32_t)bf16_rne(r[4 * t + 1]) << 16),
                                    (uint32_t)bf16_rne(r[4 * t + 2]) | ((uint32_t)bf16_rne(r[4 * t + 3]) << 16)};
                     const int col = 32 * (ly.g0 + q) + 8 * t + 4 * ((threadIdx.x >> 5) & 1);
-                    *reinterpret_cast<uint2*>(stage + row * BN + col) = w2;
+                    *reinterpret_cast<uint2*>(stage + row * YS + col) = w2;
                 }
         }
     });
@@ -1059,7 +1064,7 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
         if (r < valid) {
             const int f = a.src[row0 + r];
             if (f >= 0) {
-                const uint4 v = *reinterpret_cast<const uint4*>(stage + r * BN + part * 8);
+                const uint4 v = *reinterpret_cast<const uint4*>(stage + r * YS + part * 8);
                 *reinterpret_cast<uint4*>(a.comb + (size_t)f * a.H + nb * BN + part * 8) = v;
             }
         }
