@@ -16,14 +16,12 @@ namespace mega_moe {
 constexpr int COMBINE_THREADS = 128;
 constexpr int COMBINE_COLS = COMBINE_THREADS * 8;   // columns per workgroup
 
+// Two floats as packed BF16 (lo in bits 0-15), rounded to nearest even, NaN
+// kept as a quiet NaN (one v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    auto rne = [](float f) -> uint32_t {
-        uint32_t u = __float_as_uint(f);
-        if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-        u += 0x7fffu + ((u >> 16) & 1u);
-        return u >> 16;
-    };
-    return rne(lo) | (rne(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __global__ void __launch_bounds__(COMBINE_THREADS)

@@ -298,11 +298,14 @@ __device__ __forceinline__ float lane_row_scale(const uint8_t* sf_rows, int slic
     return __builtin_bit_cast(float, *reinterpret_cast<const int*>(sf_rows + 4 * r));
 }
 
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// Two floats as packed BF16 (lo in bits 0-15), rounded to nearest even, NaN
+// kept as a quiet NaN: one v_cvt_pk_bf16_f32 (measured on MI355X identical
+// to integer round-to-nearest-even of the bit pattern for every class of
+// input, subnormals and ties included).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // silu(g) * u of one output: the optional activation clamp of both values
@@ -1051,8 +1054,7 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const v16f& r = acc[j][q];
-                    const uint2 w2{(uint32_t)bf16_rne(r[4 * t]) | ((uint32_t)bf16_rne(r[4 * t + 1]) << 16),
-                                   (uint32_t)bf16_rne(r[4 * t + 2]) | ((uint32_t)bf16_rne(r[4 * t + 3]) << 16)};
+                    const uint2 w2{pack_bf16x2(r[4 * t], r[4 * t + 1]), pack_bf16x2(r[4 * t + 2], r[4 * t + 3])};
                     const int col = 32 * (ly.g0 + q) + 8 * t + 4 * ((threadIdx.x >> 5) & 1);
                     *reinterpret_cast<uint2*>(stage + row * YS + col) = w2;
                 }
