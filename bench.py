@@ -128,9 +128,10 @@ def cpu_baseline(name, inp, work):
 EXACT_PATH_PEAK_TFLOPS = 1.0 / ((2.0 / 3.0) / 2500.0 + (1.0 / 3.0) / 5000.0)
 
 
-def measure(name, args, torch, B, S, RS):
-    """Times `args.steps` forwards of one workload after `args.warmup`
-    untimed ones; returns (inputs, work, result dict)."""
+def prepare(name, args, torch, B, S, RS):
+    """Inputs of one workload generated on the host and resident on the GPU,
+    a layer handle sized for it, and the host-side look-ups of its result:
+    everything that is not a step happens before the first step."""
     inp = S.make_inputs(name)
     work = work_of(inp)
     wkeys = ("w1_fp4", "w1_e8", "w2_fp4", "w2_e8") if work["mx"] else ("w1", "w1_sf", "w2", "w2_sf")
@@ -148,6 +149,24 @@ def measure(name, args, torch, B, S, RS):
         fwd(dev["x"], dev["x_sf"], dev["topk_idx"], dev["topk_weights"], dev[wkeys[0]],
             dev[wkeys[1]], dev[wkeys[2]], dev[wkeys[3]], y)
 
+    # calibrated HBM bytes per launch from the committed counter summary of
+    # this workload; None when the library sources changed since it was taken
+    # (hashing the sources takes long enough that, done between two timed
+    # workloads, it let the GPU's clock drop)
+    traffic = RS.read_traffic(os.path.join(ROOT, "profiles", f"moe_expert_ffn_{name}_hbm_traffic.txt"), name)
+    return dict(name=name, inp=inp, work=work, dev=dev, y=y, layer=layer, plan=plan, step=step,
+                traffic=traffic)
+
+
+def measure(ctx, args, torch, B):
+    """Times `args.steps` forwards of a prepared workload after `args.warmup`
+    untimed ones.  Only the raw times are kept here (in ctx); `result` builds
+    the result after every workload is timed, since its first call costs tens
+    of milliseconds of one-time host work (numpy's first median and the
+    like), and a GPU idle that long between two workloads starts the second
+    on a lower clock (measured: a 35 ms gap put the decode expert kernel at
+    263-267 us against 243-245 without it)."""
+    name, layer, step = ctx["name"], ctx["layer"], ctx["step"]
     for _ in range(args.warmup):
         step()
     status = layer.status()
@@ -171,8 +190,14 @@ def measure(name, args, torch, B, S, RS):
     status = layer.status()
     if status:
         raise SystemExit(f"{name}: device error bits {status:#x}")
-    layer.close()
-    del dev, y
+    ctx["times"] = (t0, t1, t2, t3, prof)
+
+
+def result(ctx, args):
+    """The result dict of a measured workload: (inputs, work, result)."""
+    name, inp, work, plan = ctx["name"], ctx["inp"], ctx["work"], ctx["plan"]
+    t0, t1, t2, t3, prof = ctx["times"]
+    T, H = inp["x"].shape
 
     ms = (t1 - t0) * 1e3 / args.steps
     s = ms / 1e3
@@ -190,10 +215,7 @@ def measure(name, args, torch, B, S, RS):
         roof = {"bound": "hbm", "achieved": work["compulsory_bytes"] / (expert_ms / 1e3) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    # calibrated HBM bytes per launch from the committed counter summary of
-    # this workload; None when the library sources changed since it was taken
-    roof["traffic"] = RS.read_traffic(
-        os.path.join(ROOT, "profiles", f"moe_expert_ffn_{name}_hbm_traffic.txt"), name)
+    roof["traffic"] = ctx["traffic"]
     roof["algorithmic_bytes"] = work["compulsory_bytes"]
     roof["algorithmic_flops"] = work["flops"]
     roof["intermediate_bytes"] = work["intermediate_bytes"]
@@ -259,16 +281,33 @@ def main():
 
     name = args.workload
     pre = None
-    if name == "decode" and not args.no_prefill:
+    with_prefill = name == "decode" and not args.no_prefill
+    # Both workloads' inputs are generated and uploaded before any timing:
+    # building the decode inputs on the host takes seconds, and a GPU left
+    # idle that long starts the next steps on a lower clock (measured on
+    # MI355X: decode expert kernels of 280-300 us for the first 20 steps after
+    # a 2 s pause, 242 us steady, 245 us from the first step when they follow
+    # the prefill steps directly).
+    # Nothing is freed until every workload is timed either: after the
+    # prefill buffers were freed the next 60 decode steps ran at 260-311 us
+    # per expert kernel (245-249 us with them kept); and between the two
+    # workloads nothing runs on the host but the timing itself.
+    pctx = prepare("prefill", args, torch, B, S, RS) if with_prefill else None
+    ctx = prepare(name, args, torch, B, S, RS)
+    if with_prefill:
         # the compute-bound half of the metric: the 8192-token prefill batch,
         # the same number of warm-up and timed steps.  It runs first, so the
-        # decode steps are then timed on a GPU already under load, as in a
-        # running model: after an idle period the GPU takes about 50 decode
-        # steps (15 ms) to reach its steady clock (measured on MI355X:
-        # 282-306 us per expert kernel over the first 50 steps, 266-267 us
-        # after), which a few warm-up steps alone would time instead.
-        _, _, pre = measure("prefill", args, torch, B, S, RS)
-    inp, work, res = measure(name, args, torch, B, S, RS)
+        # decode steps are then timed on a GPU under load, as in a running
+        # model, rather than on one ramping up from idle.
+        measure(pctx, args, torch, B)
+    measure(ctx, args, torch, B)
+    if with_prefill:
+        _, _, pre = result(pctx, args)
+    inp, work, res = result(ctx, args)
+    for c in (pctx, ctx):
+        if c is not None:
+            c["layer"].close()
+            c.clear()
     out = {
         "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
