@@ -340,7 +340,14 @@ __device__ __forceinline__ float dpp_move(float x) {
 template <int MS, int BNT, int WF = W_FP8>
 struct Cfg {
     static constexpr bool MX = WF == W_MXFP4;
-    static constexpr int BM = 32 * MS;                    // pool rows per tile
+    static constexpr int PBM = 32 * MS;                   // pool rows per pool block
+    // 128-row FP8 tiles on 128 columns hold one more 32-row slice: an expert's
+    // last pool block, when it has at most 32 rows, joins the tile of the
+    // block before it, so that its weights stream once (the LDS of this
+    // configuration has room for the slice; the others do not)
+    static constexpr int XS = MS == 4 && BNT == 128 && !MX ? 1 : 0;
+    static constexpr int SL = MS + XS;                    // 32-row slices per tile
+    static constexpr int BM = 32 * SL;                    // tile rows (at most)
     static constexpr int BN = BNT;                        // output columns per tile
     static constexpr int NW = BN / 32;                    // waves per workgroup
     static constexpr int NT = 64 * NW;                    // threads per workgroup
@@ -395,6 +402,9 @@ struct Cfg {
     static_assert((A_BLK + B_BLK) % NW == 0 && A_BLK % NW == 0, "row blocks per wave");
     static_assert(!MX || BN == 128, "MXFP4 weights use 128-column tiles");
     static_assert(WAIT < 64, "vmcnt range");
+    // the extra slice's loads are skipped on tiles without it, so the number
+    // of loads per step varies: only the full wait of a two-stage ring allows that
+    static_assert(XS == 0 || S == 2, "extra slice needs the two-stage ring");
     static_assert(WPC * LDS_BYTES <= 160 * 1024, "LDS per CU");
     static_assert(BM * YS * 2 <= S * STAGE && BM * HS * 4 <= S * STAGE, "epilogue buffers");
 };
@@ -444,6 +454,7 @@ struct Loader {
     int wsc_voff;
     int w;
     int sf_step;     // bytes between the scale groups of consecutive steps
+    bool xs_on;      // the tile has rows in its extra slice (more than PBM rows)
 
     // ra: activation rows (row_a bytes each), rb: weight rows (row_b bytes),
     // rs: activation scales, rw: UE8M0 scale rows of the weight rows (row_w
@@ -453,10 +464,13 @@ struct Loader {
     // one float per row (row stride row_s bytes, step kb at byte 4 kb).  L2
     // tiles read the pool in order (arow unused) and its pool-minor scales
     // (row stride P).
+    // rows: the tile's rows; the activation rows of the extra slice load only
+    // when it has some (a tile of at most PBM rows issues what a PBM-row
+    // configuration would)
     __device__ Loader(__amdgpu_buffer_rsrc_t ra_, __amdgpu_buffer_rsrc_t rb_, int row_a, int row_b,
-                      __amdgpu_buffer_rsrc_t rs_, int P, __amdgpu_buffer_rsrc_t rw_, int row_w,
+                      __amdgpu_buffer_rsrc_t rs_, int P, __amdgpu_buffer_rsrc_t rw_, int row_w, int rows,
                       const int* arow = nullptr, int row_s = 0)
-        : ra(ra_), rb(rb_), rs(rs_), rw(rw_) {
+        : ra(ra_), rb(rb_), rs(rs_), rw(rw_), xs_on(rows > C::PBM) {
         const int lane = threadIdx.x & 63;
         w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
@@ -477,7 +491,7 @@ struct Loader {
         }
         if constexpr (HALVES == 1) {
             // one scale per lane: rows [w*BM/NW, (w+1)*BM/NW) of the tile
-            const int n = w * (C::BM / C::NW) + (lane & (C::BM / C::NW - 1));
+            const int n = w * (C::BM / C::NW) + min(lane, C::BM / C::NW - 1);
             sf_voff = arow[n] * row_s;
             sf_step = 4;
         } else {
@@ -498,8 +512,12 @@ struct Loader {
 #pragma unroll
         for (int j = 0; j < PT; ++j) {
             if (real || lane == 0) {
-                if (j < C::A_J) dma16<AUX_ACT>(ra, stage + (C::NW * j + w) * 1024, voff[j], soff_a);
-                else dma16<AUX_W>(rb, stage + (C::NW * j + w) * 1024, voff[j], soff_b);
+                if (j < C::A_J) {
+                    if (j < C::A_J - C::XS || xs_on)
+                        dma16<AUX_ACT>(ra, stage + (C::NW * j + w) * 1024, voff[j], soff_a);
+                } else {
+                    dma16<AUX_W>(rb, stage + (C::NW * j + w) * 1024, voff[j], soff_b);
+                }
             }
         }
         if constexpr (HALVES == 1) {
@@ -558,19 +576,26 @@ __device__ __forceinline__ void k_loop(const Loader<MS, BNT, HALVES, WF>& ld, co
 // is split 2 slices x 2 column groups per wave, so a slice's A operand and a
 // column group's B operand are read and converted once for two output
 // blocks; any other tile gives wave w column group w over all active slices,
-// so no wave idles on a ragged tile.
+// so no wave idles on a ragged tile.  A 160-row tile (ACT 5) is the 128-row
+// grid plus slice 4, which each wave computes for its first column group
+// g(0): the upper waves take their two groups in the other order, so that
+// the four waves' first groups are the four groups of the tile.
 template <int MS, int BNT, int ACT>
 struct Lay {
-    static constexpr bool GRID = MS == 4 && ACT == 4;
-    static constexpr int NJ = GRID ? 2 : ACT;     // 32-row slices per wave
+    static constexpr bool GRID = MS == 4 && ACT >= 4;
+    static constexpr int NJ = GRID ? 2 : ACT;     // 32-row slices per wave (grid part)
     static constexpr int NG = GRID ? 2 : 1;       // 32-column groups per wave
+    static constexpr int XJ = GRID ? ACT - 4 : 0; // extra slices (slice 4, group g(0))
     static constexpr int WC = Cfg<MS, BNT>::NW / 2;   // column-group pairs (GRID)
-    int s0, g0;
+    int s0, g0, flip;
     __device__ Lay() {
         const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         s0 = GRID ? 2 * (w / WC) : 0;
         g0 = GRID ? 2 * (w % WC) : w;
+        flip = XJ > 0 ? (w / WC) & 1 : 0;
     }
+    // the wave's column group q (0 .. NG-1)
+    __device__ int g(int q) const { return g0 + (q ^ flip); }
     // the 128-row weight scale block of this wave's column groups
     __device__ int sblock() const { return g0 >> 2; }
 };
@@ -580,14 +605,17 @@ struct IntTag {
     static constexpr int value = N;
 };
 
-// Runs fn(IntTag<act>) for the active slice count (1..MS).
-template <int MS, typename Fn>
+// Runs fn(IntTag<act>) for the active slice count (1..SL).
+template <int SL, typename Fn>
 __device__ __forceinline__ void dispatch_act(int act, Fn&& fn) {
-    if constexpr (MS >= 4) {
+    if constexpr (SL >= 5) {
+        if (act == 5) { fn(IntTag<5>{}); return; }
+    }
+    if constexpr (SL >= 4) {
         if (act == 4) { fn(IntTag<4>{}); return; }
         if (act == 3) { fn(IntTag<3>{}); return; }
     }
-    if constexpr (MS >= 2) {
+    if constexpr (SL >= 2) {
         if (act == 2) { fn(IntTag<2>{}); return; }
     }
     fn(IntTag<1>{});
@@ -604,7 +632,7 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
     const int H = a.H;
     const int KB = H / BK;
     const size_t P = a.P_cap;
-    const int act = min(MS, (valid + 31) / 32);
+    const int act = min(C::SL, (valid + 31) / 32);
     const size_t wrow0 = (size_t)e * (2 * a.I) + (size_t)nb * BN;     // first stored W1 row
 
     if constexpr (!C::MX) {
@@ -635,7 +663,7 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
         make_rsrc(a.w1 + wrow0 * row_b, (uint32_t)(BN * row_b)), H, row_b,
         make_rsrc(a.x_sf, (uint32_t)((size_t)a.T * KB * 4)), (int)P,
         make_rsrc(C::MX ? a.w1_e8 + wrow0 * (H / 32) : nullptr, C::MX ? (uint32_t)(BN * (H / 32)) : 0u),
-        H / 32, lds.tile() + 4, KB * 4);
+        H / 32, valid, lds.tile() + 4, KB * 4);
     // MXFP4: smallest and largest block scale this lane converted (reported
     // when outside 2^-23 .. 2^13, where the F16 conversion stops being exact)
     float sc_lo = 1.0f, sc_hi = 1.0f;
@@ -650,7 +678,7 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
     constexpr int HS = C::HS;                                           // h row stride (floats)
     float* hbuf = reinterpret_cast<float*>(lds.stage(0));              // [BM][HS]
 
-    dispatch_act<MS>(act, [&](auto tag) {
+    dispatch_act<C::SL>(act, [&](auto tag) {
         constexpr int ACT = decltype(tag)::value;
         using LY = Lay<MS, BNT, ACT>;
         const LY ly;
@@ -659,6 +687,7 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
         for (int j = 0; j < LY::NJ; ++j)
 #pragma unroll
             for (int q = 0; q < LY::NG; ++q) acc[j][q] = v16f{};
+        v16f accx = v16f{};   // slice 4 of a 160-row tile, column group g(0)
 
         k_loop(ld, lds, KB, [&](const uint8_t* stg, int kb) {
             const uint8_t* sfa = stg + C::OFF_SF;
@@ -670,9 +699,9 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
 #pragma unroll
                 for (int q = 0; q < LY::NG; ++q) {
                     if constexpr (C::WSC_BLOCK)
-                        wsc[q] = lane_wsc<16>(lds.wsb((kb >> 2) & 1) + 4 * (kb & 3), ly.g0 + q);
+                        wsc[q] = lane_wsc<16>(lds.wsb((kb >> 2) & 1) + 4 * (kb & 3), ly.g(q));
                     else
-                        wsc[q] = lane_wsc(stg + C::OFF_WSC, ly.g0 + q);
+                        wsc[q] = lane_wsc(stg + C::OFF_WSC, ly.g(q));
                 }
                 v16f d[LY::NJ][LY::NG];
                 if constexpr (LY::GRID) {
@@ -680,7 +709,7 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                     v4i ra[2][LY::NJ];
                     auto read_pair = [&](int buf, int m) {
 #pragma unroll
-                        for (int q = 0; q < LY::NG; ++q) rb[buf][q] = fp4_pair_raw(stg + C::OFF_B, ly.g0 + q, m);
+                        for (int q = 0; q < LY::NG; ++q) rb[buf][q] = fp4_pair_raw(stg + C::OFF_B, ly.g(q), m);
 #pragma unroll
                         for (int j = 0; j < LY::NJ; ++j) ra[buf][j] = frag_pair_raw(stg, ly.s0 + j, m);
                     };
@@ -744,27 +773,51 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                 // is converted and fed to four independent MFMA chains, so
                 // the LDS latency overlaps the matrix work
                 static_assert(LY::NG + LY::NJ == 4, "2 x 2 wave blocks");
+                if constexpr (LY::XJ > 0) {
+                    // slice 4 times column group g(0) first, as its own chain
+                    // over the eight parts (the order of every other chain),
+                    // folded before the grid's four chains start: at most
+                    // four chains are live at a time
+                    v16f dx;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const v4i rb = frag_pair_raw(stg + C::OFF_B, ly.g(0), m);
+                        const v4i ra = frag_pair_raw(stg, 4, m);
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            dx = mfma_f16(f16_of_pair(rb, h), f16_of_pair(ra, h), m == 0 && h == 0 ? zero : dx);
+                    }
+                    accx = __builtin_elementwise_fma(dx, v16f(lane_row_scale(sfa, 4) * sw), accx);
+                    // (kept apart from the grid below, whose reads the
+                    // scheduler would otherwise hoist into this chain)
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 v16f d[LY::NJ][LY::NG];
-                v4i raw[2][4];
+                // (a 160-row tile reads each pair when it is used: its fifth
+                // slice's accumulator takes the registers of the look-ahead)
+                constexpr int LA = LY::XJ > 0 ? 0 : 1;
+                v4i raw[1 + LA][4];
                 auto read_pair = [&](v4i* dst, int m) {
 #pragma unroll
-                    for (int q = 0; q < LY::NG; ++q) dst[q] = frag_pair_raw(stg + C::OFF_B, ly.g0 + q, m);
+                    for (int q = 0; q < LY::NG; ++q) dst[q] = frag_pair_raw(stg + C::OFF_B, ly.g(q), m);
 #pragma unroll
                     for (int j = 0; j < LY::NJ; ++j) dst[LY::NG + j] = frag_pair_raw(stg, ly.s0 + j, m);
                 };
                 read_pair(raw[0], 0);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    if (m < 3) read_pair(raw[(m + 1) & 1], m + 1);
+                    const int cb = LA ? m & 1 : 0;
+                    if (LA && m < 3) read_pair(raw[(m + 1) & LA], m + 1);
+                    if (!LA && m > 0) read_pair(raw[0], m);
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const bool first = m == 0 && h == 0;
                         v8h b16[LY::NG];
 #pragma unroll
-                        for (int q = 0; q < LY::NG; ++q) b16[q] = f16_of_pair(raw[m & 1][q], h);
+                        for (int q = 0; q < LY::NG; ++q) b16[q] = f16_of_pair(raw[cb][q], h);
 #pragma unroll
                         for (int j = 0; j < LY::NJ; ++j) {
-                            const v8h a16 = f16_of_pair(raw[m & 1][LY::NG + j], h);
+                            const v8h a16 = f16_of_pair(raw[cb][LY::NG + j], h);
 #pragma unroll
                             for (int q = 0; q < LY::NG; ++q)
                                 d[j][q] = mfma_f16(b16[q], a16, first ? zero : d[j][q]);
@@ -778,6 +831,7 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                     for (int q = 0; q < LY::NG; ++q)
                         acc[j][q] = __builtin_elementwise_fma(d[j][q], v16f(svw), acc[j][q]);
                 }
+
             } else {
                 // one column group: its B operand converted once per step,
                 // then one MFMA chain per active slice, interleaved
@@ -803,25 +857,25 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
         // lane, and each lane writes 4 consecutive outputs at a time.
         auto write_h = [&](auto fast) {
             constexpr bool FAST = decltype(fast)::value != 0;
-#pragma unroll
-            for (int j = 0; j < LY::NJ; ++j) {
-                const int row = 32 * (ly.s0 + j) + (threadIdx.x & 31);
+            // the 32 x 32 block r of slice s, column group g
+            auto put = [&](const v16f& r, int s, int g) {
+                const int row = 32 * s + (threadIdx.x & 31);
                 const float wt = lds.row_w()[row];
 #pragma unroll
-                for (int q = 0; q < LY::NG; ++q) {
+                for (int half = 0; half < 2; ++half) {
+                    float hv[4];
 #pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        float hv[4];
-#pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            hv[v] = silu_up<FAST>(acc[j][q][8 * half + v], acc[j][q][8 * half + 4 + v],
-                                                  a.act_clamp) * wt;
-                        const int col = 16 * (ly.g0 + q) + 8 * half + 4 * ((threadIdx.x >> 5) & 1);
-                        *reinterpret_cast<float4*>(hbuf + row * HS + col) =
-                            float4{hv[0], hv[1], hv[2], hv[3]};
-                    }
+                    for (int v = 0; v < 4; ++v)
+                        hv[v] = silu_up<FAST>(r[8 * half + v], r[8 * half + 4 + v], a.act_clamp) * wt;
+                    const int col = 16 * g + 8 * half + 4 * ((threadIdx.x >> 5) & 1);
+                    *reinterpret_cast<float4*>(hbuf + row * HS + col) = float4{hv[0], hv[1], hv[2], hv[3]};
                 }
-            }
+            };
+#pragma unroll
+            for (int j = 0; j < LY::NJ; ++j)
+#pragma unroll
+                for (int q = 0; q < LY::NG; ++q) put(acc[j][q], ly.s0 + j, ly.g(q));
+            if constexpr (LY::XJ > 0) put(accx, 4, ly.g(0));
         };
         if (a.fast_math) write_h(IntTag<1>{});
         else write_h(IntTag<0>{});
@@ -835,7 +889,7 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
     // BN/32 threads per row, 16 outputs each; the 4 of one 64-output scale
     // group are consecutive lanes (NT and BN/32 are multiples of 4)
     constexpr int PPR = BN / 32;
-    for (int t = threadIdx.x; t < PPR * BM; t += NT) {
+    for (int t = threadIdx.x; t < PPR * 32 * act; t += NT) {
         const int r = t / PPR, part = t % PPR;
         const float4* src4 = reinterpret_cast<const float4*>(hbuf + r * HS + 16 * part);
         float hv[16];
@@ -934,7 +988,7 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
     const int I = a.I;
     const int KB = I / BK;
     const size_t P = a.P_cap;
-    const int act = min(MS, (valid + 31) / 32);
+    const int act = min(C::SL, (valid + 31) / 32);
 
     const size_t wrow0 = (size_t)e * a.H + (size_t)nb * BN;         // first W2 row
     if constexpr (!C::MX) {
@@ -974,15 +1028,15 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
     const Loader<MS, BNT, 2, WF> ld(
         make_rsrc(a.l2_acts + (size_t)row0 * I, (uint32_t)valid * I),
         make_rsrc(a.w2 + wrow0 * row_b, (uint32_t)(BN * row_b)), I, row_b,
-        make_rsrc(a.l2_sf + row0, (uint32_t)(((2 * KB - 1) * P + BM) * 4)), (int)P,
+        make_rsrc(a.l2_sf + row0, (uint32_t)(((2 * KB - 1) * P + valid) * 4)), (int)P,
         make_rsrc(C::MX ? a.w2_e8 + wrow0 * (I / 32) : nullptr, C::MX ? (uint32_t)(BN * (I / 32)) : 0u),
-        I / 32);
+        I / 32, valid);
 
     const v16f zero = v16f{};
     constexpr int YS = C::YS;
     uint16_t* stage = reinterpret_cast<uint16_t*>(lds.stage(0));  // BF16 [BM][YS] after the k loop
 
-    dispatch_act<MS>(act, [&](auto tag) {
+    dispatch_act<C::SL>(act, [&](auto tag) {
         constexpr int ACT = decltype(tag)::value;
         using LY = Lay<MS, BNT, ACT>;
         const LY ly;
@@ -991,6 +1045,7 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
         for (int j = 0; j < LY::NJ; ++j)
 #pragma unroll
             for (int q = 0; q < LY::NG; ++q) acc[j][q] = v16f{};
+        v16f accx = v16f{};   // slice 4 of a 160-row tile, column group g(0)
 
         k_loop(ld, lds, KB, [&](const uint8_t* stg, int kb) {
             const uint8_t* sfa = stg + C::OFF_SF;
@@ -1003,11 +1058,11 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
 #pragma unroll
                 for (int q = 0; q < LY::NG; ++q) {
                     if constexpr (C::WSC_BLOCK)
-                        wsc[q] = lane_wsc<16>(lds.wsb((kb >> 2) & 1) + 4 * (kb & 3), ly.g0 + q);
+                        wsc[q] = lane_wsc<16>(lds.wsb((kb >> 2) & 1) + 4 * (kb & 3), ly.g(q));
                     else
-                        wsc[q] = lane_wsc(stg + C::OFF_WSC, ly.g0 + q);
-                    fb[q][0] = fp4_half_raw(stg + C::OFF_B, ly.g0 + q, 0);
-                    fb[q][1] = fp4_half_raw(stg + C::OFF_B, ly.g0 + q, 1);
+                        wsc[q] = lane_wsc(stg + C::OFF_WSC, ly.g(q));
+                    fb[q][0] = fp4_half_raw(stg + C::OFF_B, ly.g(q), 0);
+                    fb[q][1] = fp4_half_raw(stg + C::OFF_B, ly.g(q), 1);
                 }
                 Frag fa[LY::NJ];
                 float sa[LY::NJ][2];
@@ -1034,23 +1089,35 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
             const float sw = lds.w_sf()[ly.sblock() * KB + kb];
             Frag fb[LY::NG];
 #pragma unroll
-            for (int q = 0; q < LY::NG; ++q) fb[q] = read_frag2(stg + C::OFF_B, ly.g0 + q);
-            Frag fa[LY::NJ];
-            float svw[LY::NJ][2];
+            for (int q = 0; q < LY::NG; ++q) fb[q] = read_frag2(stg + C::OFF_B, ly.g(q));
+            Frag fa[LY::NJ + LY::XJ];
+            float svw[LY::NJ + LY::XJ][2];
 #pragma unroll
-            for (int j = 0; j < LY::NJ; ++j) {
-                fa[j] = read_frag2(stg, ly.s0 + j);
-                svw[j][0] = lane_row_scale(sfa, ly.s0 + j) * sw;
-                svw[j][1] = lane_row_scale(sfa + 4 * BM, ly.s0 + j) * sw;
+            for (int j = 0; j < LY::NJ + LY::XJ; ++j) {
+                const int sl = j < LY::NJ ? ly.s0 + j : 4;
+                fa[j] = read_frag2(stg, sl);
+                svw[j][0] = lane_row_scale(sfa, sl) * sw;
+                svw[j][1] = lane_row_scale(sfa + 4 * BM, sl) * sw;
             }
-            // product i: half i / (NJ NG), slice (i / NG) % NJ, group i % NG
-            constexpr int NB = 2 * LY::NJ * LY::NG;
+            // product i < NB0: half i / (NJ NG), slice (i / NG) % NJ, group
+            // i % NG; then slice 4 with group g(0), half i - NB0
+            constexpr int NB0 = 2 * LY::NJ * LY::NG;
+            constexpr int NB = NB0 + 2 * LY::XJ;
             prod_fold_pipeline<NB>(
                 [&](int i) {
+                    if constexpr (LY::XJ > 0) {
+                        if (i >= NB0) return mfma_f8(fb[0].h[i - NB0], fa[LY::NJ].h[i - NB0], zero);
+                    }
                     const int hh = i / (LY::NJ * LY::NG), j = (i / LY::NG) % LY::NJ, q = i % LY::NG;
                     return mfma_f8(fb[q].h[hh], fa[j].h[hh], zero);
                 },
                 [&](int i, const v16f& d) {
+                    if constexpr (LY::XJ > 0) {
+                        if (i >= NB0) {
+                            accx = __builtin_elementwise_fma(d, v16f(svw[LY::NJ][i - NB0]), accx);
+                            return;
+                        }
+                    }
                     const int hh = i / (LY::NJ * LY::NG), j = (i / LY::NG) % LY::NJ, q = i % LY::NG;
                     acc[j][q] = __builtin_elementwise_fma(d, v16f(svw[j][hh]), acc[j][q]);
                 });
@@ -1059,22 +1126,23 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
         // ---- epilogue: BF16 partials, staged so each route row is stored whole ----
         // (transposed blocks: register v of lane l is column 8(v/4) + 4(l/32)
         // + v%4 of the group for row l%32; four registers = 8 bytes of a row)
+        auto put = [&](const v16f& r, int s, int g) {
+            const int row = 32 * s + (threadIdx.x & 31);
 #pragma unroll
-        for (int j = 0; j < LY::NJ; ++j) {
-            const int row = 32 * (ly.s0 + j) + (threadIdx.x & 31);
+            for (int t = 0; t < 4; ++t) {
+                const uint2 w2{pack_bf16x2(r[4 * t], r[4 * t + 1]), pack_bf16x2(r[4 * t + 2], r[4 * t + 3])};
+                const int col = 32 * g + 8 * t + 4 * ((threadIdx.x >> 5) & 1);
+                *reinterpret_cast<uint2*>(stage + row * YS + col) = w2;
+            }
+        };
 #pragma unroll
-            for (int q = 0; q < LY::NG; ++q)
+        for (int j = 0; j < LY::NJ; ++j)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const v16f& r = acc[j][q];
-                    const uint2 w2{pack_bf16x2(r[4 * t], r[4 * t + 1]), pack_bf16x2(r[4 * t + 2], r[4 * t + 3])};
-                    const int col = 32 * (ly.g0 + q) + 8 * t + 4 * ((threadIdx.x >> 5) & 1);
-                    *reinterpret_cast<uint2*>(stage + row * YS + col) = w2;
-                }
-        }
+            for (int q = 0; q < LY::NG; ++q) put(acc[j][q], ly.s0 + j, ly.g(q));
+        if constexpr (LY::XJ > 0) put(accx, 4, ly.g(0));
     });
     __syncthreads();
-    for (int q = threadIdx.x; q < BM * (BN / 8); q += NT) {
+    for (int q = threadIdx.x; q < 32 * act * (BN / 8); q += NT) {
         const int r = q / (BN / 8), part = q % (BN / 8);
         if (r < valid) {
             const int f = a.src[row0 + r];
@@ -1094,7 +1162,7 @@ __global__ void __launch_bounds__((Cfg<MS, BNT, WF>::NT)) __attribute__((amdgpu_
 moe_expert_ffn(MoeArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg<MS, BNT, WF>::LDS_BYTES];
     const Lds<MS, BNT, WF> lds{smem};
-    constexpr int BM = Cfg<MS, BNT, WF>::BM;
+    constexpr int PBM = Cfg<MS, BNT, WF>::PBM;
     // XCC_ID hardware register, bits [3:0]
     const int xcd = (__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xf) % a.n_xcd;
     const int G = a.xcd_group;
@@ -1140,11 +1208,23 @@ moe_expert_ffn(MoeArgs a) {
         if (is_l1) tile_coords(u, first, cnt, a.nb1, G, a.n_major, expert_of, block_start, pb, nb);
         else tile_coords(u, first, cnt, a.nb2, G, a.n_major, expert_of, block_start, pb, nb);
         const int e = __builtin_amdgcn_readfirstlane(a.pb_expert[pb]);
-        const int m_local = pb - __builtin_amdgcn_readfirstlane(a.mb_start[e]);
-        const int row0 = __builtin_amdgcn_readfirstlane(a.offsets[e]) + m_local * BM;
-        const int valid = min(BM, __builtin_amdgcn_readfirstlane(a.counts[e]) - m_local * BM);
-        if (is_l1) l1_tile(a, lds, e, pb, row0, valid, nb);
-        else l2_tile(a, lds, e, pb, row0, valid, nb, v != xcd);
+        const int mb0 = __builtin_amdgcn_readfirstlane(a.mb_start[e]);
+        const int m_local = pb - mb0;
+        const int row0 = __builtin_amdgcn_readfirstlane(a.offsets[e]) + m_local * PBM;
+        const int count = __builtin_amdgcn_readfirstlane(a.counts[e]);
+        int valid = min(PBM, count - m_local * PBM);
+        if constexpr (Cfg<MS, BNT, WF>::XS > 0) {
+            const int nblk = __builtin_amdgcn_readfirstlane(a.mb_start[e + 1]) - mb0;
+            if (nblk >= 2 && count - (nblk - 1) * PBM <= 32 * Cfg<MS, BNT, WF>::XS) {
+                // the last block joins the tile of the block before it
+                if (m_local == nblk - 1) valid = 0;
+                else if (m_local == nblk - 2) valid = count - m_local * PBM;
+            }
+        }
+        if (valid > 0) {
+            if (is_l1) l1_tile(a, lds, e, pb, row0, valid, nb);
+            else l2_tile(a, lds, e, pb, row0, valid, nb, v != xcd);
+        }
         __syncthreads();
     }
 }

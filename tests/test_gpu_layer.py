@@ -93,6 +93,48 @@ def test_tiles_taken_across_xcds_match_oracle(name):
             run.close()
 
 
+# Per-expert route counts that reach every case of the 160-row tiles of the
+# 128-row tier: a last pool block of 1 and of 32 rows that joins the block
+# before it (129, 160 routes), one of 33 rows that does not (161), a
+# three-block expert whose last block joins (288 = 2 x 128 + 32), a single
+# short block with no block before it (33), an expert without routes, and
+# one inactive slot.
+MERGE_COUNTS = (129, 160, 161, 288, 33, 0)
+
+
+def _merge_case():
+    if "merge" not in _cache:
+        k = 2
+        T = (sum(MERGE_COUNTS) + 1 + k - 1) // k
+        wl = S.custom("merge", tokens=T, hidden=256, intermediate=128,
+                      experts=len(MERGE_COUNTS), topk=k, seed=21, weight_seed=22)
+        inp = S.make_inputs(wl)
+        ids = np.repeat(np.arange(len(MERGE_COUNTS)), MERGE_COUNTS)
+        ids = np.concatenate([ids, np.full(T * k - ids.size, -1)])
+        np.random.Generator(np.random.PCG64(23)).shuffle(ids)
+        inp["topk_idx"] = ids.reshape(T, k).astype(inp["topk_idx"].dtype)
+        ref = moe.forward(inp)
+        assert tuple(ref["counts"]) == MERGE_COUNTS
+        _cache["merge"] = (inp, ref)
+    return _cache["merge"]
+
+
+@pytest.mark.parametrize("l2_n_major", [0, 1])
+@pytest.mark.parametrize("split", [0, 4])
+def test_merged_tail_blocks_match_oracle(l2_n_major, split):
+    # an expert's last pool block of at most 32 rows is computed by the tile
+    # of the block before it (160 rows at most, one weight stream); both tile
+    # orders (N-major also takes L2 tiles across XCDs) and the split phases
+    inp, ref = _merge_case()
+    run = G.Runner(inp, block_m=128, l2_n_major=l2_n_major, split_l2_cus=split)
+    try:
+        assert run.forward() == 0
+        err = _compare_all(inp, ref, run, f"merge l2_n_major {l2_n_major} split {split}")
+        print(f"merge l2_n_major {l2_n_major} split {split}: y rel frobenius {err:.2e}")
+    finally:
+        run.close()
+
+
 def _biting_clamp(inp):
     """A clamp below about a third of the |gate| and |up| values of expert 0."""
     acc = moe.l1_gemm(inp["x"][:8], inp["x_sf"][:8], inp["w1"][0], inp["w1_sf"][0])
