@@ -420,9 +420,9 @@ struct Lds {
     __device__ float* w_sf() const { return reinterpret_cast<float*>(base + C::OFF_TILE); }
     __device__ float* row_w() const { return w_sf() + MAX_W_SF * C::NSB; }   // top-k weight per row (L1)
     // [0] the dequeued tile, [1] the XCD whose queue it came from, [3] 1 for
-    // an L1 tile, [4, 4 + BM) the L1 tile's x rows,
-    // [4 + BM, 4 + 2 BM) each row's top-k weight exponent offset (row_w holds
-    // w * 2^TINY_W_SHIFT for the rows where it is set)
+    // an L1 tile, [4, 4 + BM) the L1 tile's x rows or the L2 tile's routes
+    // (-1 past its valid rows), [4 + BM, 4 + 2 BM) 1 for the L1 rows whose
+    // row_w holds the top-k weight times 2^64 (a tiny weight), else 0
     __device__ int* tile() const { return reinterpret_cast<int*>(row_w() + C::BM); }
     __device__ int* row_tiny() const { return tile() + 4 + C::BM; }
 };
@@ -996,6 +996,9 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
         const float* wsf = a.w2_sf + ((size_t)e * a.nb2 + nb) * C::NSB * KB;
         for (int i = threadIdx.x; i < C::NSB * KB; i += NT) lds.w_sf()[i] = wsf[i];
     }
+    // each row's route (-1 past the valid rows), for the epilogue's stores: read
+    // now, alongside the scales, instead of one dependent load per store round
+    for (int r = threadIdx.x; r < BM; r += NT) lds.tile()[4 + r] = r < valid ? a.src[row0 + r] : -1;
     // wait until every L1 tile of this pool block has published.  A tile of
     // this XCD's own range reads the block from this XCD's L2, where its L1
     // tiles left it.  A tile taken from another XCD's queue waits for the
@@ -1144,12 +1147,10 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
     __syncthreads();
     for (int q = threadIdx.x; q < 32 * act * (BN / 8); q += NT) {
         const int r = q / (BN / 8), part = q % (BN / 8);
-        if (r < valid) {
-            const int f = a.src[row0 + r];
-            if (f >= 0) {
-                const uint4 v = *reinterpret_cast<const uint4*>(stage + r * YS + part * 8);
-                *reinterpret_cast<uint4*>(a.comb + (size_t)f * a.H + nb * BN + part * 8) = v;
-            }
+        const int f = lds.tile()[4 + r];
+        if (f >= 0) {
+            const uint4 v = *reinterpret_cast<const uint4*>(stage + r * YS + part * 8);
+            *reinterpret_cast<uint4*>(a.comb + (size_t)f * a.H + nb * BN + part * 8) = v;
         }
     }
 }
