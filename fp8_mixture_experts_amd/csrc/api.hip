@@ -57,7 +57,7 @@ struct Layout {
 };
 
 enum {
-    L_COUNTS, L_OFFSETS, L_MBSTART, L_PBEXP, L_SLOTMAP, L_SRC, L_CHIST, L_CBASE,
+    L_COUNTS, L_OFFSETS, L_MBSTART, L_PBEXP, L_PBREC, L_SLOTMAP, L_SRC, L_CHIST, L_CBASE,
     L_L1ACTS, L_L1SF, L_L1W, L_L2ACTS, L_L2SF, L_COMB, L_READY, L_XCDINFO, L_CTRL,
     L_COUNT
 };
@@ -125,6 +125,7 @@ Layout make_layout(const mega_moe_config& c) {
     sz[L_OFFSETS] = (E + 1) * 4;
     sz[L_MBSTART] = (E + 1) * 4;
     sz[L_PBEXP] = L.PB_cap * 4;
+    sz[L_PBREC] = L.PB_cap * 16;
     sz[L_SLOTMAP] = L.R_max * 4;
     sz[L_SRC] = L.P_cap * 4;
     sz[L_CHIST] = L.chunks_max * E * 4;
@@ -197,6 +198,7 @@ void bind_workspace(MoeArgs& a, const mega_moe_config& cfg, const Layout& L, uin
     a.offsets = (int32_t*)(w + L.off[L_OFFSETS]);
     a.mb_start = (int32_t*)(w + L.off[L_MBSTART]);
     a.pb_expert = (int32_t*)(w + L.off[L_PBEXP]);
+    a.pb_rec = (int32_t*)(w + L.off[L_PBREC]);
     a.slot_map = (int32_t*)(w + L.off[L_SLOTMAP]);
     a.src = (int32_t*)(w + L.off[L_SRC]);
     a.chunk_hist = (int32_t*)(w + L.off[L_CHIST]);
@@ -507,6 +509,7 @@ static void call_args(MoeArgs& a, const mega_moe_config& cfg, int32_t T, const u
     a.n_major = p.l2_n_major;
     // cross-XCD tail balancing pays with the large batches of the N-major schedule
     a.steal = p.l2_n_major;
+    a.merge_tail = merge_tail_for(mx, p.block_m, p.block_n);
     a.xcd_group = xcd_group_for(p.block_m);
     a.num_chunks = (a.R + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK;
     a.x = x;

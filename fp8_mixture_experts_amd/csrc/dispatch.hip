@@ -142,7 +142,9 @@ __device__ void finish_counts(const MoeArgs& a, const int* s_count, int* s_off, 
         a.xcd_info[2 * tid + 1] = cnt;
     }
 
-    // expert of every pool block, and a cleared arrival counter for it
+    // expert of every pool block, a cleared arrival counter for it, and its
+    // record for the expert kernel's tile set-up: expert, first pool row, the
+    // rows its tiles compute, and its N-major group inside its XCD's range
     for (int pb = tid; pb < total_mb; pb += SCAN_THREADS) {
         int lo = 0, hi = E - 1;               // last expert with s_mb[ex] <= pb
         while (lo < hi) {
@@ -151,6 +153,18 @@ __device__ void finish_counts(const MoeArgs& a, const int* s_count, int* s_off, 
         }
         a.pb_expert[pb] = lo;
         a.ready[pb] = 0;
+        const int ex = lo, m = pb - s_mb[ex];
+        const int rows = tile_rows(m, s_mb[ex + 1] - s_mb[ex], s_count[ex], a.block_m, a.merge_tail != 0);
+        int x = 0, xlo = 0, xcnt = 0;
+        for (; x < a.n_xcd; ++x) {
+            xcd_range(total_mb, a.n_xcd, x, xlo, xcnt);
+            if (pb < xlo + xcnt) break;
+        }
+        int g0, gs;
+        tile_group(pb, xlo, xcnt, a.xcd_group, a.n_major != 0, [&](int) { return ex; },
+                   [&](int ee) { return s_mb[ee]; }, g0, gs);
+        *reinterpret_cast<int4*>(a.pb_rec + 4 * (size_t)pb) =
+            int4{ex, s_off[ex] + m * a.block_m, rows, (g0 << 8) | gs};
     }
 }
 

@@ -345,7 +345,7 @@ struct Cfg {
     // last pool block, when it has at most 32 rows, joins the tile of the
     // block before it, so that its weights stream once (the LDS of this
     // configuration has room for the slice; the others do not)
-    static constexpr int XS = MS == 4 && BNT == 128 && !MX ? 1 : 0;
+    static constexpr int XS = merge_tail_for(MX, 32 * MS, BNT) ? 1 : 0;
     static constexpr int SL = MS + XS;                    // 32-row slices per tile
     static constexpr int BM = 32 * SL;                    // tile rows (at most)
     static constexpr int BN = BNT;                        // output columns per tile
@@ -449,7 +449,9 @@ struct Loader {
     static constexpr int PT = C::PT;
     static constexpr int Q = 4 * HALVES * C::BM / C::NW;  // scale bytes per wave
     __amdgpu_buffer_rsrc_t ra, rb, rs, rw;
-    int voff[PT];
+    int voff[C::A_J];   // the wave's activation blocks
+    int voff_b;         // its first weight block; block A_J + i lies i * bstep bytes further
+    int bstep;
     int sf_voff;
     int wsc_voff;
     int w;
@@ -473,21 +475,23 @@ struct Loader {
         : ra(ra_), rb(rb_), rs(rs_), rw(rw_), xs_on(rows > C::PBM) {
         const int lane = threadIdx.x & 63;
         w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        // (consecutive weight blocks of a wave are NW blocks, 32 FP8 or 64
+        // MXFP4 rows, apart, with the same swizzle: one offset and a stride)
 #pragma unroll
-        for (int j = 0; j < PT; ++j) {
-            const int b = C::NW * j + w;
-            if (j < C::A_J) {
-                const int n = 8 * b + (lane >> 3);                  // activation row
-                int src_row = n;
-                if constexpr (HALVES == 1) src_row = arow[n];
-                voff[j] = src_row * row_a + 16 * ((lane & 7) ^ row_swz(n));
-            } else if constexpr (C::MX) {
-                const int n = 16 * (b - C::A_BLK) + (lane >> 2);    // MXFP4 weight row
-                voff[j] = n * row_b + 16 * ((lane & 3) ^ swz4(n));
-            } else {
-                const int n = 8 * (b - C::A_BLK) + (lane >> 3);     // FP8 weight row
-                voff[j] = n * row_b + 16 * ((lane & 7) ^ row_swz(n));
-            }
+        for (int j = 0; j < C::A_J; ++j) {
+            const int n = 8 * (C::NW * j + w) + (lane >> 3);           // activation row
+            int src_row = n;
+            if constexpr (HALVES == 1) src_row = arow[n];
+            voff[j] = src_row * row_a + 16 * ((lane & 7) ^ row_swz(n));
+        }
+        if constexpr (C::MX) {
+            const int n = 16 * w + (lane >> 2);                        // MXFP4 weight row
+            voff_b = n * row_b + 16 * ((lane & 3) ^ swz4(n));
+            bstep = 16 * C::NW * row_b;
+        } else {
+            const int n = 8 * w + (lane >> 3);                         // FP8 weight row
+            voff_b = n * row_b + 16 * ((lane & 7) ^ row_swz(n));
+            bstep = 8 * C::NW * row_b;
         }
         if constexpr (HALVES == 1) {
             // one scale per lane: rows [w*BM/NW, (w+1)*BM/NW) of the tile
@@ -516,7 +520,7 @@ struct Loader {
                     if (j < C::A_J - C::XS || xs_on)
                         dma16<AUX_ACT>(ra, stage + (C::NW * j + w) * 1024, voff[j], soff_a);
                 } else {
-                    dma16<AUX_W>(rb, stage + (C::NW * j + w) * 1024, voff[j], soff_b);
+                    dma16<AUX_W>(rb, stage + (C::NW * j + w) * 1024, voff_b, soff_b + (j - C::A_J) * bstep);
                 }
             }
         }
@@ -859,7 +863,11 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
             constexpr bool FAST = decltype(fast)::value != 0;
             // the 32 x 32 block r of slice s, column group g
             auto put = [&](const v16f& r, int s, int g) {
-                const int row = 32 * s + (threadIdx.x & 31);
+                // (the lane's row offset is formed here, not kept in a register
+                // from the kernel's start: this kernel uses all 256)
+                int lane = threadIdx.x & 31;
+                asm volatile("" : "+v"(lane));
+                const int row = 32 * s + lane;
                 const float wt = lds.row_w()[row];
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
@@ -1163,7 +1171,6 @@ __global__ void __launch_bounds__((Cfg<MS, BNT, WF>::NT)) __attribute__((amdgpu_
 moe_expert_ffn(MoeArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg<MS, BNT, WF>::LDS_BYTES];
     const Lds<MS, BNT, WF> lds{smem};
-    constexpr int PBM = Cfg<MS, BNT, WF>::PBM;
     // XCC_ID hardware register, bits [3:0]
     const int xcd = (__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xf) % a.n_xcd;
     const int G = a.xcd_group;
@@ -1176,13 +1183,16 @@ moe_expert_ffn(MoeArgs a) {
     // the XCD (xcd + q - 1) % n_xcd, past that done.
     int q = a.phase == 2 ? 1 : 0;
     const int q_end = a.phase == 0 && a.steal ? 1 + a.n_xcd : 2;
+    // this XCD's range of pool blocks (fixed for the call)
+    const int own_first = __builtin_amdgcn_readfirstlane(a.xcd_info[2 * xcd]);
+    const int own_cnt = __builtin_amdgcn_readfirstlane(a.xcd_info[2 * xcd + 1]);
     for (;;) {
         if (threadIdx.x == 0) {
             int u = -1, v = xcd, l1 = 0;
             while (q < q_end) {
                 if (q == 0) {
                     const int t = atomicAdd(&a.ctrl->next_tile[xcd], 1);
-                    if (t < a.xcd_info[2 * xcd + 1] * a.nb1) { u = t; l1 = 1; break; }
+                    if (t < own_cnt * a.nb1) { u = t; l1 = 1; break; }
                     q = a.phase == 1 ? q_end : 1;
                 } else {
                     v = (xcd + q - 1) % a.n_xcd;
@@ -1195,38 +1205,38 @@ moe_expert_ffn(MoeArgs a) {
             lds.tile()[1] = v;
             lds.tile()[3] = l1;
         }
+        // one barrier per tile here: every wave has finished the previous tile
+        // (whose LDS the next one overwrites), and the dequeued tile is
+        // visible.  Thread 0 writes it again only after the tile's own first
+        // barrier (or the one below for a tile with no rows), which every wave
+        // reaches after reading it.
         __syncthreads();
         const int u = __builtin_amdgcn_readfirstlane(lds.tile()[0]);
         const int v = __builtin_amdgcn_readfirstlane(lds.tile()[1]);
         const bool is_l1 = __builtin_amdgcn_readfirstlane(lds.tile()[3]) != 0;
-        __syncthreads();
         if (u < 0) break;
-        const int first = __builtin_amdgcn_readfirstlane(a.xcd_info[2 * v]);
-        const int cnt = __builtin_amdgcn_readfirstlane(a.xcd_info[2 * v + 1]);
-        const auto expert_of = [&](int p) { return __builtin_amdgcn_readfirstlane(a.pb_expert[p]); };
-        const auto block_start = [&](int e) { return __builtin_amdgcn_readfirstlane(a.mb_start[e]); };
-        int pb, nb;
-        if (is_l1) tile_coords(u, first, cnt, a.nb1, G, a.n_major, expert_of, block_start, pb, nb);
-        else tile_coords(u, first, cnt, a.nb2, G, a.n_major, expert_of, block_start, pb, nb);
-        const int e = __builtin_amdgcn_readfirstlane(a.pb_expert[pb]);
-        const int mb0 = __builtin_amdgcn_readfirstlane(a.mb_start[e]);
-        const int m_local = pb - mb0;
-        const int row0 = __builtin_amdgcn_readfirstlane(a.offsets[e]) + m_local * PBM;
-        const int count = __builtin_amdgcn_readfirstlane(a.counts[e]);
-        int valid = min(PBM, count - m_local * PBM);
-        if constexpr (Cfg<MS, BNT, WF>::XS > 0) {
-            const int nblk = __builtin_amdgcn_readfirstlane(a.mb_start[e + 1]) - mb0;
-            if (nblk >= 2 && count - (nblk - 1) * PBM <= 32 * Cfg<MS, BNT, WF>::XS) {
-                // the last block joins the tile of the block before it
-                if (m_local == nblk - 1) valid = 0;
-                else if (m_local == nblk - 2) valid = count - m_local * PBM;
-            }
+        // the tile from its pool block's record (expert, first pool row, rows,
+        // N-major group), written by the dispatch
+        const int first = v == xcd ? own_first : __builtin_amdgcn_readfirstlane(a.xcd_info[2 * v]);
+        const int nbs = is_l1 ? a.nb1 : a.nb2;
+        const int pq = first + u / nbs;
+        int g0 = pq, gs = 1;
+        if (a.n_major && G > 1) {
+            const int grp = __builtin_amdgcn_readfirstlane(a.pb_rec[4 * pq + 3]);
+            g0 = grp >> 8;
+            gs = grp & 255;
         }
+        int pb, nb;
+        tile_in_group(u, first, nbs, g0, gs, pb, nb);
+        const int e = __builtin_amdgcn_readfirstlane(a.pb_rec[4 * pb]);
+        const int row0 = __builtin_amdgcn_readfirstlane(a.pb_rec[4 * pb + 1]);
+        const int valid = __builtin_amdgcn_readfirstlane(a.pb_rec[4 * pb + 2]);
         if (valid > 0) {
             if (is_l1) l1_tile(a, lds, e, pb, row0, valid, nb);
             else l2_tile(a, lds, e, pb, row0, valid, nb, v != xcd);
+        } else {
+            __syncthreads();   // (a block taken by the tile before it)
         }
-        __syncthreads();
     }
 }
 

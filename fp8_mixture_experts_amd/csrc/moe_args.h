@@ -38,6 +38,8 @@ struct MoeArgs {
     int32_t w_fmt;      // 0: FP8 weights with float block scales, 1: MXFP4 weights
     int32_t phase;      // expert kernel: 0 L1 and L2 tiles, 1 L1 tiles only, 2 L2 tiles only
     int32_t steal;      // phase 0: workgroups out of tiles take L2 tiles queued on other XCDs
+    int32_t merge_tail; // 1: an expert's last pool block of at most 32 rows joins the tile of
+                        // the block before it (the expert kernel's 128-row FP8 tiles)
 
     // inputs (caller-owned)
     const uint8_t* x;
@@ -57,6 +59,8 @@ struct MoeArgs {
     int32_t* offsets;     // [E+1]
     int32_t* mb_start;    // [E+1] first pool block of each expert
     int32_t* pb_expert;   // [PB_cap] expert of each pool block
+    int32_t* pb_rec;      // [PB_cap][4] per pool block: expert, first pool row, rows its
+                          // tiles compute (tile_rows), N-major group (first block << 8 | size)
     int32_t* slot_map;    // [R]
     int32_t* src;         // [P_cap]
     int32_t* chunk_hist;  // [num_chunks, E]
