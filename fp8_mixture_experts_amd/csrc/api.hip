@@ -57,7 +57,8 @@ struct Layout {
 };
 
 enum {
-    L_COUNTS, L_OFFSETS, L_MBSTART, L_PBEXP, L_PBREC, L_SLOTMAP, L_SRC, L_CHIST, L_CBASE,
+    L_COUNTS, L_OFFSETS, L_MBSTART, L_PBEXP, L_PBREC, L_SLOTMAP, L_SRC, L_POOLW, L_CHIST,
+    L_CBASE,
     L_L1ACTS, L_L1SF, L_L1W, L_L2ACTS, L_L2SF, L_COMB, L_READY, L_XCDINFO, L_CTRL,
     L_COUNT
 };
@@ -128,6 +129,7 @@ Layout make_layout(const mega_moe_config& c) {
     sz[L_PBREC] = L.PB_cap * 16;
     sz[L_SLOTMAP] = L.R_max * 4;
     sz[L_SRC] = L.P_cap * 4;
+    sz[L_POOLW] = L.P_cap * 4;
     sz[L_CHIST] = L.chunks_max * E * 4;
     sz[L_CBASE] = L.chunks_max * E * 4;
     // the pool copies exist only when the configuration keeps the pool
@@ -201,6 +203,7 @@ void bind_workspace(MoeArgs& a, const mega_moe_config& cfg, const Layout& L, uin
     a.pb_rec = (int32_t*)(w + L.off[L_PBREC]);
     a.slot_map = (int32_t*)(w + L.off[L_SLOTMAP]);
     a.src = (int32_t*)(w + L.off[L_SRC]);
+    a.pool_w = (float*)(w + L.off[L_POOLW]);
     a.chunk_hist = (int32_t*)(w + L.off[L_CHIST]);
     a.chunk_base = (int32_t*)(w + L.off[L_CBASE]);
     a.l1_acts = w + L.off[L_L1ACTS];

@@ -256,6 +256,7 @@ moe_dispatch_small(MoeArgs a) {
         __syncthreads();
         const int f = round * SCAN_THREADS + tid;
         const int e = f < a.R ? a.topk_idx[f] : -1;
+        const float wf = f < a.R ? a.topk_w[f] : 0.0f;
         const bool valid = e >= 0 && e < E;
         int n_same;
         const int rank = wave_rank(valid ? e : E, key_bits, &n_same);
@@ -266,6 +267,7 @@ moe_dispatch_small(MoeArgs a) {
             for (int w = 0; w < wave; ++w) slot += wcnt[w][e];
             a.slot_map[f] = slot;
             a.src[slot] = f;
+            a.pool_w[slot] = wf;
         } else if (f < a.R) {
             a.slot_map[f] = -1;
         }
@@ -299,6 +301,7 @@ moe_dispatch_scatter(MoeArgs a) {
         __syncthreads();
         const int f = c * DISPATCH_CHUNK + round * DISPATCH_THREADS + tid;
         int e = f < a.R ? a.topk_idx[f] : -1;
+        const float wf = f < a.R ? a.topk_w[f] : 0.0f;
         const bool valid = e >= 0 && e < E;
         int n_same;
         const int rank = wave_rank(valid ? e : E, key_bits, &n_same);
@@ -310,6 +313,7 @@ moe_dispatch_scatter(MoeArgs a) {
             const int slot = a.chunk_base[(size_t)c * E + e] + before;
             a.slot_map[f] = slot;
             a.src[slot] = f;
+            a.pool_w[slot] = wf;
         } else if (f < a.R) {
             a.slot_map[f] = -1;
         }

@@ -646,15 +646,18 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
     }
     // the tile's rows come straight from x: tile row r < valid is route
     // src[row0 + r] = t*k + j, which reads row t of x and x_sf and takes the
-    // top-k weight topk_w[t*k + j]; padding rows point one row past the end
-    // of x, where the buffer loads return zeros
+    // top-k weight topk_w[t*k + j] (from the dispatch's copy of it per pool
+    // row); padding rows point one row past the end of x, where the buffer
+    // loads return zeros
     // A top-k weight below 2^-60 (an underflowed softmax) is kept as
     // w * 2^64: h = silu(g) * u * w would otherwise fall below float32's
     // normal range and lose the bits its codes need; the factor comes back
     // out of the row's scales, exactly, in the quantisation below.
     for (int r = threadIdx.x; r < BM; r += NT) {
+        // (every row below valid is a routed row; its weight comes from the
+        // dispatch's per-row copy, so the two loads go out together)
         const int f = r < valid ? a.src[row0 + r] : -1;
-        const float wt = f >= 0 ? a.topk_w[f] : 0.0f;
+        const float wt = r < valid ? a.pool_w[row0 + r] : 0.0f;
         const bool tiny = fabsf(wt) < 0x1p-60f;
         lds.row_w()[r] = tiny ? wt * 0x1p64f : wt;
         lds.row_tiny()[r] = tiny ? 1 : 0;

@@ -63,6 +63,7 @@ struct MoeArgs {
                           // tiles compute (tile_rows), N-major group (first block << 8 | size)
     int32_t* slot_map;    // [R]
     int32_t* src;         // [P_cap]
+    float* pool_w;        // [P_cap] the top-k weight of each routed pool row (others unset)
     int32_t* chunk_hist;  // [num_chunks, E]
     int32_t* chunk_base;  // [num_chunks, E]
     uint8_t* l1_acts;     // [P_cap, H]  pool copy of the routed rows (kept pool only)
