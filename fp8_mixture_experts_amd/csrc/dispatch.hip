@@ -155,11 +155,9 @@ __device__ void finish_counts(const MoeArgs& a, const int* s_count, int* s_off, 
         a.ready[pb] = 0;
         const int ex = lo, m = pb - s_mb[ex];
         const int rows = tile_rows(m, s_mb[ex + 1] - s_mb[ex], s_count[ex], a.block_m, a.merge_tail != 0);
-        int x = 0, xlo = 0, xcnt = 0;
-        for (; x < a.n_xcd; ++x) {
-            xcd_range(total_mb, a.n_xcd, x, xlo, xcnt);
-            if (pb < xlo + xcnt) break;
-        }
+        const int x = xcd_of_block(pb, total_mb, a.n_xcd);
+        const int xlo = total_mb * x / a.n_xcd;
+        const int xcnt = total_mb * (x + 1) / a.n_xcd - xlo;
         int g0, gs;
         tile_group(pb, xlo, xcnt, a.xcd_group, a.n_major != 0, [&](int) { return ex; },
                    [&](int ee) { return s_mb[ee]; }, g0, gs);
@@ -224,6 +222,7 @@ __device__ __forceinline__ int wave_rank(int key, int key_bits, int* peers_count
 // wave counts in LDS across waves, a running base per expert across rounds).
 constexpr int SMALL_CHUNKS = 4;
 constexpr int SMALL_WAVES = SCAN_THREADS / 64;
+constexpr int SMALL_ROUNDS = SMALL_CHUNKS * DISPATCH_CHUNK / SCAN_THREADS;
 
 __global__ void __launch_bounds__(SCAN_THREADS)
 moe_dispatch_small(MoeArgs a) {
@@ -236,11 +235,22 @@ moe_dispatch_small(MoeArgs a) {
     const int wave = tid >> 6;
     const int E = a.E;
 
+    // every route's expert and top-k weight, read once (at most SMALL_CHUNKS
+    // rounds of SCAN_THREADS routes) for the histogram and the ranking
+    int re[SMALL_ROUNDS];
+    float rw[SMALL_ROUNDS];
+#pragma unroll
+    for (int r = 0; r < SMALL_ROUNDS; ++r) {
+        const int f = r * SCAN_THREADS + tid;
+        re[r] = f < a.R ? a.topk_idx[f] : -1;
+        rw[r] = f < a.R ? a.topk_w[f] : 0.0f;
+    }
     for (int e = tid; e < E; e += SCAN_THREADS) s_count[e] = 0;
     __syncthreads();
     bool bad = false;
-    for (int f = tid; f < a.R; f += SCAN_THREADS) {
-        const int e = a.topk_idx[f];
+#pragma unroll
+    for (int r = 0; r < SMALL_ROUNDS; ++r) {
+        const int e = re[r];
         if (e >= 0 && e < E) atomicAdd(&s_count[e], 1);
         else if (e >= E) bad = true;
     }
@@ -251,12 +261,14 @@ moe_dispatch_small(MoeArgs a) {
     int key_bits = 0;
     while ((1 << key_bits) <= E) ++key_bits;
     // s_off becomes the running base of each expert's next slot
-    for (int round = 0; round * SCAN_THREADS < a.R; ++round) {
+#pragma unroll
+    for (int round = 0; round < SMALL_ROUNDS; ++round) {
+        if (round * SCAN_THREADS >= a.R) break;
         for (int i = tid; i < SMALL_WAVES * E; i += SCAN_THREADS) wcnt[i / E][i % E] = 0;
         __syncthreads();
         const int f = round * SCAN_THREADS + tid;
-        const int e = f < a.R ? a.topk_idx[f] : -1;
-        const float wf = f < a.R ? a.topk_w[f] : 0.0f;
+        const int e = re[round];
+        const float wf = rw[round];
         const bool valid = e >= 0 && e < E;
         int n_same;
         const int rank = wave_rank(valid ? e : E, key_bits, &n_same);

@@ -23,6 +23,13 @@ __host__ __device__ inline void xcd_range(int total_mb, int n_xcd, int x, int& l
     cnt = (int)((int64_t)total_mb * (x + 1) / n_xcd) - lo;
 }
 
+// The XCD whose range holds pool block pb (0 <= pb < total_mb): the largest x
+// with floor(total_mb * x / n_xcd) <= pb, in 32-bit arithmetic (total_mb *
+// n_xcd stays far below 2^31).
+__host__ __device__ inline int xcd_of_block(int pb, int total_mb, int n_xcd) {
+    return ((pb + 1) * n_xcd - 1) / total_mb;
+}
+
 // Tile u of XCD range [first, first + cnt) with nbs N blocks: pool block pb
 // and N block nb.  The range's pool blocks form groups: each run of one
 // expert's blocks inside the range, cut into pieces of at most G blocks
