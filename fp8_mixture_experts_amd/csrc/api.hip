@@ -57,8 +57,7 @@ struct Layout {
 };
 
 enum {
-    L_COUNTS, L_OFFSETS, L_MBSTART, L_PBEXP, L_PBREC, L_SLOTMAP, L_SRC, L_POOLW, L_CHIST,
-    L_CBASE,
+    L_COUNTS, L_OFFSETS, L_PBREC, L_SLOTMAP, L_SRC, L_POOLW, L_CHIST, L_CBASE,
     L_L1ACTS, L_L1SF, L_L1W, L_L2ACTS, L_L2SF, L_COMB, L_READY, L_XCDINFO, L_CTRL,
     L_COUNT
 };
@@ -124,8 +123,6 @@ Layout make_layout(const mega_moe_config& c) {
     int64_t sz[L_COUNT];
     sz[L_COUNTS] = E * 4;
     sz[L_OFFSETS] = (E + 1) * 4;
-    sz[L_MBSTART] = (E + 1) * 4;
-    sz[L_PBEXP] = L.PB_cap * 4;
     sz[L_PBREC] = L.PB_cap * 16;
     sz[L_SLOTMAP] = L.R_max * 4;
     sz[L_SRC] = L.P_cap * 4;
@@ -198,8 +195,6 @@ void bind_workspace(MoeArgs& a, const mega_moe_config& cfg, const Layout& L, uin
     a.n_xcd = n_xcd;
     a.counts = (int32_t*)(w + L.off[L_COUNTS]);
     a.offsets = (int32_t*)(w + L.off[L_OFFSETS]);
-    a.mb_start = (int32_t*)(w + L.off[L_MBSTART]);
-    a.pb_expert = (int32_t*)(w + L.off[L_PBEXP]);
     a.pb_rec = (int32_t*)(w + L.off[L_PBREC]);
     a.slot_map = (int32_t*)(w + L.off[L_SLOTMAP]);
     a.src = (int32_t*)(w + L.off[L_SRC]);

@@ -110,13 +110,11 @@ __device__ void finish_counts(const MoeArgs& a, const int* s_count, int* s_off, 
         a.counts[e] = cnt;
         if (a.recv_stats) a.recv_stats[e] += cnt;
         a.offsets[e] = off;
-        a.mb_start[e] = mb0;
     }
     if (tid == 0) {
         s_off[E] = total_rows;
         s_mb[E] = total_mb;
         a.offsets[E] = total_rows;
-        a.mb_start[E] = total_mb;
         a.ctrl->total_mb = total_mb;
         for (int x = 0; x < MAX_XCD; ++x) {
             a.ctrl->next_tile[x] = 0;
@@ -142,16 +140,15 @@ __device__ void finish_counts(const MoeArgs& a, const int* s_count, int* s_off, 
         a.xcd_info[2 * tid + 1] = cnt;
     }
 
-    // expert of every pool block, a cleared arrival counter for it, and its
-    // record for the expert kernel's tile set-up: expert, first pool row, the
-    // rows its tiles compute, and its N-major group inside its XCD's range
+    // a cleared arrival counter for every pool block, and its record for the
+    // expert kernel's tile set-up: expert, first pool row, the rows its tiles
+    // compute, and its N-major group inside its XCD's range
     for (int pb = tid; pb < total_mb; pb += SCAN_THREADS) {
         int lo = 0, hi = E - 1;               // last expert with s_mb[ex] <= pb
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (s_mb[mid] <= pb) lo = mid; else hi = mid - 1;
         }
-        a.pb_expert[pb] = lo;
         a.ready[pb] = 0;
         const int ex = lo, m = pb - s_mb[ex];
         const int rows = tile_rows(m, s_mb[ex + 1] - s_mb[ex], s_count[ex], a.block_m, a.merge_tail != 0);

@@ -57,8 +57,6 @@ struct MoeArgs {
     // workspace (handle-owned)
     int32_t* counts;      // [E]
     int32_t* offsets;     // [E+1]
-    int32_t* mb_start;    // [E+1] first pool block of each expert
-    int32_t* pb_expert;   // [PB_cap] expert of each pool block
     int32_t* pb_rec;      // [PB_cap][4] per pool block: expert, first pool row, rows its
                           // tiles compute (tile_rows), N-major group (first block << 8 | size)
     int32_t* slot_map;    // [R]

@@ -248,7 +248,8 @@ int mega_moe_plan(const mega_moe_config* cfg, int32_t num_tokens, mega_moe_plan_
  * The expert kernel's tile order for a plan (a host-side query; needs no GPU).
  * block_start[e] is expert e's first pool block, block_start[E] the number M
  * of pool blocks (host array of num_experts + 1 non-decreasing entries from
- * 0; a forward call's values are the mb_start view).  The M pool blocks are
+ * 0; for a forward call, block_start[e + 1] - block_start[e] is
+ * ceil(counts[e] / plan->block_m)).  The M pool blocks are
  * split into n_xcd contiguous ranges, XCD x taking [x*M/n_xcd,
  * (x+1)*M/n_xcd); that XCD's workgroups take the tiles of its range from its
  * own queue, all L1 tiles (phase 1) before the L2 tiles (phase 2), each tile
