@@ -695,6 +695,17 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
 #pragma unroll
             for (int q = 0; q < LY::NG; ++q) acc[j][q] = v16f{};
         v16f accx = v16f{};   // slice 4 of a 160-row tile, column group g(0)
+        // FP8 weights on the 2 x 2 wave grid: the raw products of the previous
+        // step and their scales, folded into acc at the start of the next step
+        // (zero before the first, so that fold adds nothing)
+        v16f dp[LY::NJ][LY::NG];
+        float svp[LY::NJ];
+#pragma unroll
+        for (int j = 0; j < LY::NJ; ++j) {
+            svp[j] = 0.0f;
+#pragma unroll
+            for (int q = 0; q < LY::NG; ++q) dp[j][q] = v16f{};
+        }
 
         k_loop(ld, lds, KB, [&](const uint8_t* stg, int kb) {
             const uint8_t* sfa = stg + C::OFF_SF;
@@ -799,11 +810,11 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                     // scheduler would otherwise hoist into this chain)
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                v16f d[LY::NJ][LY::NG];
-                // (a 160-row tile reads each pair when it is used: its fifth
-                // slice's accumulator takes the registers of the look-ahead)
-                constexpr int LA = LY::XJ > 0 ? 0 : 1;
-                v4i raw[1 + LA][4];
+                // this step's scales, for the fold at the start of the next step
+                float svw[LY::NJ];
+#pragma unroll
+                for (int j = 0; j < LY::NJ; ++j) svw[j] = lane_row_scale(sfa, ly.s0 + j) * sw;
+                v4i raw[2][4];
                 auto read_pair = [&](v4i* dst, int m) {
 #pragma unroll
                     for (int q = 0; q < LY::NG; ++q) dst[q] = frag_pair_raw(stg + C::OFF_B, ly.g(q), m);
@@ -813,9 +824,10 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                 read_pair(raw[0], 0);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const int cb = LA ? m & 1 : 0;
-                    if (LA && m < 3) read_pair(raw[(m + 1) & LA], m + 1);
-                    if (!LA && m > 0) read_pair(raw[0], m);
+                    const int cb = m & 1;
+                    if (m < 3) read_pair(raw[(m + 1) & 1], m + 1);
+                    // (the look-ahead reads stay ahead of this pair's work)
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const bool first = m == 0 && h == 0;
@@ -826,18 +838,20 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                         for (int j = 0; j < LY::NJ; ++j) {
                             const v8h a16 = f16_of_pair(raw[cb][LY::NG + j], h);
 #pragma unroll
-                            for (int q = 0; q < LY::NG; ++q)
-                                d[j][q] = mfma_f16(b16[q], a16, first ? zero : d[j][q]);
+                            for (int q = 0; q < LY::NG; ++q) {
+                                // the previous step's product of this chain is
+                                // folded just before the chain restarts, so the
+                                // adds overlap this step's LDS reads and first
+                                // products instead of trailing the last ones
+                                if (first)
+                                    acc[j][q] = __builtin_elementwise_fma(dp[j][q], v16f(svp[j]), acc[j][q]);
+                                dp[j][q] = mfma_f16(b16[q], a16, first ? zero : dp[j][q]);
+                            }
                         }
                     }
                 }
 #pragma unroll
-                for (int j = 0; j < LY::NJ; ++j) {
-                    const float svw = lane_row_scale(sfa, ly.s0 + j) * sw;
-#pragma unroll
-                    for (int q = 0; q < LY::NG; ++q)
-                        acc[j][q] = __builtin_elementwise_fma(d[j][q], v16f(svw), acc[j][q]);
-                }
+                for (int j = 0; j < LY::NJ; ++j) svp[j] = svw[j];
 
             } else {
                 // one column group: its B operand converted once per step,
@@ -856,6 +870,14 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
             }
         });
 
+        if constexpr (!C::MX && LY::GRID) {
+            // the last step's products
+#pragma unroll
+            for (int j = 0; j < LY::NJ; ++j)
+#pragma unroll
+                for (int q = 0; q < LY::NG; ++q)
+                    acc[j][q] = __builtin_elementwise_fma(dp[j][q], v16f(svp[j]), acc[j][q]);
+        }
         // the k loop ended with a barrier, so the stages are free for h.  In a
         // transposed block, register v of lane l holds stored W1 row
         // 8(v/4) + 4(l/32) + v%4 of the column group for activation row l%32:
@@ -988,6 +1010,23 @@ __device__ __forceinline__ void prod_fold_pipeline(Prod&& prod, Fold&& fold) {
     }
 }
 
+// The same, but the adds of the last product are left to the caller, who gets
+// that product back and folds it at the start of the next step: fold_prev
+// (the previous step's last product) runs once product 0 is issued, so those
+// adds overlap the matrix core instead of waiting out the last product.
+template <int NB, typename Prod, typename Fold, typename FoldPrev>
+__device__ __forceinline__ v16f prod_fold_carry(Prod&& prod, Fold&& fold, FoldPrev&& fold_prev) {
+    v16f d[2];
+    d[0] = prod(0);
+    fold_prev();
+#pragma unroll
+    for (int i = 0; i + 1 < NB; ++i) {
+        d[(i + 1) & 1] = prod(i + 1);
+        fold(i, d[i & 1]);
+    }
+    return d[(NB - 1) & 1];
+}
+
 // ---------------------------------------------------------------------------
 // L2 tile: pool rows [row0, row0 + valid) of expert e, W2 N block nb.
 // ---------------------------------------------------------------------------
@@ -1060,6 +1099,17 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
 #pragma unroll
             for (int q = 0; q < LY::NG; ++q) acc[j][q] = v16f{};
         v16f accx = v16f{};   // slice 4 of a 160-row tile, column group g(0)
+        // FP8 weights: the previous step's last product and its scale (zero
+        // before the first step), and where it folds: slice 4 when the tile
+        // has one, else the last slice and group, both in the second 64-K half
+        v16f dl = v16f{};
+        float sl = 0.0f;
+        auto fold_last = [&]() {
+            if constexpr (LY::XJ > 0)
+                accx = __builtin_elementwise_fma(dl, v16f(sl), accx);
+            else
+                acc[LY::NJ - 1][LY::NG - 1] = __builtin_elementwise_fma(dl, v16f(sl), acc[LY::NJ - 1][LY::NG - 1]);
+        };
 
         k_loop(ld, lds, KB, [&](const uint8_t* stg, int kb) {
             const uint8_t* sfa = stg + C::OFF_SF;
@@ -1117,7 +1167,7 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
             // i % NG; then slice 4 with group g(0), half i - NB0
             constexpr int NB0 = 2 * LY::NJ * LY::NG;
             constexpr int NB = NB0 + 2 * LY::XJ;
-            prod_fold_pipeline<NB>(
+            dl = prod_fold_carry<NB>(
                 [&](int i) {
                     if constexpr (LY::XJ > 0) {
                         if (i >= NB0) return mfma_f8(fb[0].h[i - NB0], fa[LY::NJ].h[i - NB0], zero);
@@ -1134,8 +1184,11 @@ __device__ __forceinline__ void l2_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                     }
                     const int hh = i / (LY::NJ * LY::NG), j = (i / LY::NG) % LY::NJ, q = i % LY::NG;
                     acc[j][q] = __builtin_elementwise_fma(d, v16f(svw[j][hh]), acc[j][q]);
-                });
+                },
+                fold_last);
+            sl = LY::XJ > 0 ? svw[LY::NJ + LY::XJ - 1][1] : svw[LY::NJ - 1][1];
         });
+        if constexpr (!C::MX) fold_last();   // the last step's last product
 
         // ---- epilogue: BF16 partials, staged so each route row is stored whole ----
         // (transposed blocks: register v of lane l is column 8(v/4) + 4(l/32)
