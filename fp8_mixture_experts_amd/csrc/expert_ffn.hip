@@ -796,15 +796,20 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
                     // over the eight parts (the order of every other chain),
                     // folded before the grid's four chains start: at most
                     // four chains are live at a time
-                    v16f dx;
+                    // (all its fragment pairs read first, so that one LDS
+                    // latency precedes the chain instead of one per pair)
+                    v4i xb[4], xa[4];
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        const v4i rb = frag_pair_raw(stg + C::OFF_B, ly.g(0), m);
-                        const v4i ra = frag_pair_raw(stg, 4, m);
+                        xb[m] = frag_pair_raw(stg + C::OFF_B, ly.g(0), m);
+                        xa[m] = frag_pair_raw(stg, 4, m);
+                    }
+                    v16f dx;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
 #pragma unroll
                         for (int h = 0; h < 2; ++h)
-                            dx = mfma_f16(f16_of_pair(rb, h), f16_of_pair(ra, h), m == 0 && h == 0 ? zero : dx);
-                    }
+                            dx = mfma_f16(f16_of_pair(xb[m], h), f16_of_pair(xa[m], h), m == 0 && h == 0 ? zero : dx);
                     accx = __builtin_elementwise_fma(dx, v16f(lane_row_scale(sfa, 4) * sw), accx);
                     // (kept apart from the grid below, whose reads the
                     // scheduler would otherwise hoist into this chain)
