@@ -141,7 +141,7 @@ def prepare(name, args, torch, B, S, RS):
     y = torch.empty((T, H), dtype=torch.int16, device="cuda:0")
     layer = B.MegaMoE(work["E"], H, work["I"], work["k"], T, block_m=args.block_m,
                       block_n=args.block_n, l2_n_major=args.l2_n_major,
-                      split_l2_cus=args.split_l2_cus)
+                      split_l2_cus=args.split_l2_cus, split_l2_xcds=args.split_l2_xcds)
     plan = B.mega_moe_plan(layer.cfg, T)
     fwd = layer.forward_mxfp4 if work["mx"] else layer.forward
 
@@ -231,7 +231,7 @@ def result(ctx, args):
                    "experts": work["E"], "topk": work["k"], "routing": inp["workload"].routing,
                    "block_m": plan.block_m, "block_n": 128 if work["mx"] else plan.block_n,
                    "weights": "mxfp4" if work["mx"] else "fp8",
-                   "split_l2_cus": args.split_l2_cus,
+                   "split_l2_cus": args.split_l2_cus, "split_l2_xcds": args.split_l2_xcds,
                    "l2_n_major": plan.l2_n_major},
         "tflops": tflops, "weight_stream_gbs": wgbs,
         "pct_roofline": 100.0 * t_roof / s,
@@ -261,6 +261,8 @@ def main():
     ap.add_argument("--split-l2-cus", type=int, default=0,
                     help="run L1 and L2 tiles as two concurrent kernels, the L2 one with this "
                          "many CUs' worth of workgroups per XCD (0: one fused kernel)")
+    ap.add_argument("--split-l2-xcds", type=int, default=0,
+                    help="L1 and L2 tiles on disjoint XCD sets: the last n XCDs take the L2 tiles")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="with the decode workload, skip the prefill measurement that the "

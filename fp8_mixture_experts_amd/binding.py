@@ -40,7 +40,8 @@ class mega_moe_config(ctypes.Structure):
                 ("max_tokens", ctypes.c_int32), ("activation_clamp", ctypes.c_float),
                 ("fast_math", ctypes.c_int32), ("block_m", ctypes.c_int32),
                 ("l2_n_major", ctypes.c_int32), ("block_n", ctypes.c_int32),
-                ("split_l2_cus", ctypes.c_int32), ("keep_pool", ctypes.c_int32)]
+                ("split_l2_cus", ctypes.c_int32), ("keep_pool", ctypes.c_int32),
+                ("split_l2_xcds", ctypes.c_int32)]
 
 
 class mega_moe_plan_info(ctypes.Structure):
@@ -126,10 +127,10 @@ def _check(rc: int) -> int:
 
 def make_config(num_experts, hidden, intermediate, num_topk, max_tokens, block_m=0,
                 l2_n_major=-1, activation_clamp=math.inf, fast_math=0,
-                block_n=0, split_l2_cus=0, keep_pool=0) -> mega_moe_config:
+                block_n=0, split_l2_cus=0, keep_pool=0, split_l2_xcds=0) -> mega_moe_config:
     return mega_moe_config(num_experts, hidden, intermediate, num_topk, max_tokens,
                            activation_clamp, fast_math, block_m, l2_n_major, block_n,
-                           split_l2_cus, keep_pool)
+                           split_l2_cus, keep_pool, split_l2_xcds)
 
 
 # ---- the C entry points, one Python function each ---------------------------

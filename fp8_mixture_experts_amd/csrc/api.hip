@@ -105,6 +105,11 @@ int check_config(const mega_moe_config* c) {
                     c->split_l2_cus);
     if (c->keep_pool != 0 && c->keep_pool != 1)
         return fail(MEGA_MOE_ERR_INVALID_ARG, "keep_pool must be 0 or 1");
+    if (c->split_l2_xcds < 0 || c->split_l2_xcds >= MAX_XCD)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "split_l2_xcds must be in [0, %d), got %d", MAX_XCD,
+                    c->split_l2_xcds);
+    if (c->split_l2_xcds > 0 && c->split_l2_cus > 0)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "split_l2_cus and split_l2_xcds exclude each other");
     // the expert kernel addresses rows of x with 32-bit byte offsets
     if ((int64_t)c->max_tokens * c->hidden > ((int64_t)1 << 31) - 2 * (int64_t)c->hidden)
         return fail(MEGA_MOE_ERR_INVALID_ARG, "max_tokens * hidden must stay below 2^31");
@@ -297,6 +302,22 @@ int split_setup(mega_moe_handle* h, int l2) {
     }
     return MEGA_MOE_OK;
 }
+
+// Sets up the split phases on disjoint XCD sets.  One persistent launch
+// fills the device as usual; the workgroups of XCDs [0, n_xcd - l2_xcds) take
+// only L1 tiles and those of the other XCDs only L2 tiles, so the two phases
+// run on disjoint sets of compute units (the partition is fixed by the
+// hardware's XCC_ID, no CU mask).  The dispatch gives the pool blocks to the
+// L1 XCDs only, every pool block's output is written back through memory for
+// the L2 XCDs, and an L2 workgroup only ever waits for L1 workgroups of other
+// XCDs, which never wait: no residency assumption beyond one workgroup per XCD.
+int split_setup_xcds(mega_moe_handle* h, int l2_xcds) {
+    const int nx = h->base.n_xcd;
+    if (l2_xcds >= nx)
+        return fail(MEGA_MOE_ERR_INVALID_ARG, "split_l2_xcds %d leaves no L1 XCD of %d", l2_xcds, nx);
+    h->base.phase = PHASE_XCD_SPLIT + nx - l2_xcds;
+    return MEGA_MOE_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -434,8 +455,9 @@ int mega_moe_create(const mega_moe_config* cfg, mega_moe_handle** out) {
     }
     bind_workspace(h->base, *cfg, h->L, h->ws, h->n_xcd);
     h->last_T = 0;
-    if (cfg->split_l2_cus > 0) {
-        rc = split_setup(h, cfg->split_l2_cus);
+    if (cfg->split_l2_cus > 0 || cfg->split_l2_xcds > 0) {
+        rc = cfg->split_l2_cus > 0 ? split_setup(h, cfg->split_l2_cus)
+                                   : split_setup_xcds(h, cfg->split_l2_xcds);
         if (rc) {
             const std::string msg = g_last_error;
             hipFree(h->ws);
@@ -544,8 +566,9 @@ static int forward_impl(mega_moe_handle* h, int32_t T, const uint8_t* x, const f
     launch_dispatch(a, gather_blocks, stream);
     if (call >= 0) hipEventRecord(prof_event(h, call, 1), stream);
     if (h->split_stream[0]) {
-        // the L1 and L2 tiles as two concurrent kernels on disjoint CU sets,
-        // forked from and joined back into the caller's stream
+        // the L1 and L2 tiles as two concurrent kernels (disjoint workgroup
+        // budgets, or disjoint XCD sets), forked from and joined back into the
+        // caller's stream
         hipEventRecord(h->split_event[0], stream);
         for (int i = 0; i < 2; ++i) {
             hipStreamWaitEvent(h->split_stream[i], h->split_event[0], 0);
@@ -758,9 +781,9 @@ int mega_moe_forward_noalloc(const mega_moe_config* cfg, int32_t T, const uint8_
                              uint32_t* dev_errors, void* stream_v) {
     int rc = check_config(cfg);
     if (rc) return rc;
-    if (cfg->keep_pool || cfg->split_l2_cus)
+    if (cfg->keep_pool || cfg->split_l2_cus || cfg->split_l2_xcds)
         return fail(MEGA_MOE_ERR_INVALID_ARG,
-                    "the allocation-free forward takes neither keep_pool nor split_l2_cus");
+                    "the allocation-free forward takes neither keep_pool nor a split");
     if (T < 0 || T > cfg->max_tokens)
         return fail(MEGA_MOE_ERR_INVALID_ARG, "num_tokens %d outside [0, max_tokens=%d]", T,
                     cfg->max_tokens);

@@ -132,10 +132,12 @@ __device__ void finish_counts(const MoeArgs& a, const int* s_count, int* s_off, 
     }
 
     // Per-XCD work: XCD x takes a contiguous range of the M pool blocks
-    // (expert-major)
+    // (expert-major); with the phases on disjoint XCD sets only the L1 XCDs
+    // hold ranges
+    const int rx = range_xcds(a.phase, a.n_xcd);
     if (tid < a.n_xcd) {
-        int lo, cnt;
-        xcd_range(total_mb, a.n_xcd, tid, lo, cnt);
+        int lo = total_mb, cnt = 0;
+        if (tid < rx) xcd_range(total_mb, rx, tid, lo, cnt);
         a.xcd_info[2 * tid] = lo;
         a.xcd_info[2 * tid + 1] = cnt;
     }
@@ -152,9 +154,9 @@ __device__ void finish_counts(const MoeArgs& a, const int* s_count, int* s_off, 
         a.ready[pb] = 0;
         const int ex = lo, m = pb - s_mb[ex];
         const int rows = tile_rows(m, s_mb[ex + 1] - s_mb[ex], s_count[ex], a.block_m, a.merge_tail != 0);
-        const int x = xcd_of_block(pb, total_mb, a.n_xcd);
-        const int xlo = total_mb * x / a.n_xcd;
-        const int xcnt = total_mb * (x + 1) / a.n_xcd - xlo;
+        const int x = xcd_of_block(pb, total_mb, rx);
+        const int xlo = total_mb * x / rx;
+        const int xcnt = total_mb * (x + 1) / rx - xlo;
         int g0, gs;
         tile_group(pb, xlo, xcnt, a.xcd_group, a.n_major != 0, [&](int) { return ex; },
                    [&](int ee) { return s_mb[ee]; }, g0, gs);

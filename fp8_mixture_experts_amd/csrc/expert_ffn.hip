@@ -986,7 +986,7 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
     if (threadIdx.x == 0) {
         const uint32_t done =
             __hip_atomic_fetch_add(&a.ready[pb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
-        if (a.phase == 0 && a.steal && done == (uint32_t)a.nb1) {
+        if (((a.phase == 0 && a.steal) || a.phase >= PHASE_XCD_SPLIT) && done == (uint32_t)a.nb1) {
             // the write-back must be complete before the mark is set: the
             // compiler's own wait after the fence's write-back can be merged
             // away (it was, here), so it is written out
@@ -1241,9 +1241,15 @@ moe_expert_ffn(MoeArgs a) {
     // fused kernel (phase 0) it then takes the L2 tiles still queued on the
     // other XCDs, so that XCDs that finish early share the work of the slower
     // ones.  Thread 0 keeps the queue state: 0 own L1, 1 own L2, 2 .. n_xcd
-    // the XCD (xcd + q - 1) % n_xcd, past that done.
-    int q = a.phase == 2 ? 1 : 0;
-    const int q_end = a.phase == 0 && a.steal ? 1 + a.n_xcd : 2;
+    // the XCD (xcd + q - 1) % n_xcd, past that done.  With the phases on
+    // disjoint XCD sets (phase 3 + n) an L1 XCD's workgroups take its own L1
+    // queue only, and an L2 XCD's the L2 queues of the n L1 XCDs in turn
+    // (state q >= 1: the XCD (xcd + q - 1) % n).
+    const int nx1 = a.phase - PHASE_XCD_SPLIT;
+    const bool l2_side = a.phase == 2 || (a.phase >= PHASE_XCD_SPLIT && xcd >= nx1);
+    int q = l2_side ? 1 : 0;
+    const int q_end = a.phase >= PHASE_XCD_SPLIT ? (l2_side ? 1 + nx1 : 1)
+                                                 : (a.phase == 0 && a.steal ? 1 + a.n_xcd : 2);
     // this XCD's range of pool blocks (fixed for the call)
     const int own_first = __builtin_amdgcn_readfirstlane(a.xcd_info[2 * xcd]);
     const int own_cnt = __builtin_amdgcn_readfirstlane(a.xcd_info[2 * xcd + 1]);
@@ -1254,9 +1260,9 @@ moe_expert_ffn(MoeArgs a) {
                 if (q == 0) {
                     const int t = atomicAdd(&a.ctrl->next_tile[xcd], 1);
                     if (t < own_cnt * a.nb1) { u = t; l1 = 1; break; }
-                    q = a.phase == 1 ? q_end : 1;
+                    q = a.phase == 0 ? 1 : q_end;
                 } else {
-                    v = (xcd + q - 1) % a.n_xcd;
+                    v = (xcd + q - 1) % (a.phase >= PHASE_XCD_SPLIT ? nx1 : a.n_xcd);
                     const int t = atomicAdd(&a.ctrl->next_tile_l2[v], 1);
                     if (t < a.xcd_info[2 * v + 1] * a.nb2) { u = t; break; }
                     ++q;

@@ -8,6 +8,13 @@
 namespace mega_moe {
 
 constexpr int MAX_XCD = 16;
+constexpr int PHASE_XCD_SPLIT = 3;   // phase 3 + n: L1 tiles on XCDs [0, n), L2 tiles on the others
+
+// XCDs whose ranges hold the pool blocks: all of them, or the L1 XCDs of a
+// split on disjoint XCD sets.
+__host__ __device__ inline int range_xcds(int phase, int n_xcd) {
+    return phase >= PHASE_XCD_SPLIT ? phase - PHASE_XCD_SPLIT : n_xcd;
+}
 
 // Control record in device memory, reset by the dispatch scan of every call.
 struct MoeCtrl {
@@ -36,7 +43,11 @@ struct MoeArgs {
     float act_clamp;    // clamp of gate and up before SiLU (+inf: none)
     int32_t fast_math;  // 1: hardware exp2 and reciprocal in SiLU
     int32_t w_fmt;      // 0: FP8 weights with float block scales, 1: MXFP4 weights
-    int32_t phase;      // expert kernel: 0 L1 and L2 tiles, 1 L1 tiles only, 2 L2 tiles only
+    int32_t phase;      // expert kernel: 0 L1 and L2 tiles, 1 L1 tiles only, 2 L2 tiles only;
+                        // 3 + n (1 <= n < n_xcd): the L1 and L2 tiles on disjoint XCD sets,
+                        // the workgroups of XCDs [0, n) take only L1 tiles and the others
+                        // only L2 tiles (the dispatch then gives the pool blocks to
+                        // XCDs [0, n) only)
     int32_t steal;      // phase 0: workgroups out of tiles take L2 tiles queued on other XCDs
     int32_t merge_tail; // 1: an expert's last pool block of at most 32 rows joins the tile of
                         // the block before it (the expert kernel's 128-row FP8 tiles)

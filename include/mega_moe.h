@@ -91,6 +91,16 @@ typedef struct mega_moe_config {
                                  also copies them into the expert pool (the pages'
                                  pull into the pool, SM90 design 9.2) so that the
                                  l1_* views show them; results are the same */
+    int32_t split_l2_xcds;    /* 0: off.  n > 0: the L1 and L2 tiles run on
+                                 disjoint sets of XCDs (accelerator dies of 32 CUs)
+                                 inside the one persistent launch: the workgroups of
+                                 the last n XCDs take only L2 tiles, the others only
+                                 L1 tiles, and every pool block's L1 output is
+                                 written back through memory for the L2 set (the
+                                 green-context split of the PR357 review, sections 1
+                                 and 5.2, with partitions of whole dies).  n < the
+                                 device's XCD count (8); excludes split_l2_cus.
+                                 Results are the same */
 } mega_moe_config;
 
 typedef struct mega_moe_handle mega_moe_handle;

@@ -91,7 +91,9 @@ def test_plan_overrides():
                                 dict(block_m=32, block_n=256),
                                 dict(hidden=7296, block_n=256), dict(activation_clamp=0.0),
                                 dict(activation_clamp=-1.0), dict(activation_clamp=math.nan),
-                                dict(fast_math=2), dict(split_l2_cus=-1), dict(split_l2_cus=32)])
+                                dict(fast_math=2), dict(split_l2_cus=-1), dict(split_l2_cus=32),
+                                dict(split_l2_xcds=-1), dict(split_l2_xcds=16),
+                                dict(split_l2_cus=4, split_l2_xcds=2)])
 def test_invalid_configs_are_rejected(kw):
     assert B.mega_moe_workspace_bytes(_cfg(**kw)) == -1
     with pytest.raises(B.MegaMoEError) as ei:
@@ -241,6 +243,7 @@ def test_noalloc_forward_refusals_need_no_gpu():
     assert "scratch" in B.mega_moe_last_error()
     for cfg, n in ((_cfg(max_tokens=128, keep_pool=1), 128),
                    (_cfg(max_tokens=128, split_l2_cus=4), 128),
+                   (_cfg(max_tokens=128, split_l2_xcds=2), 128),
                    (_cfg(max_tokens=128), 129)):
         with pytest.raises(B.MegaMoEError) as ei:
             B.mega_moe_forward_noalloc(cfg, n, *tensors, None, None)

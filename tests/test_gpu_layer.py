@@ -120,13 +120,15 @@ def _merge_case():
 
 
 @pytest.mark.parametrize("l2_n_major", [0, 1])
-@pytest.mark.parametrize("split", [0, 4])
+@pytest.mark.parametrize("split", [0, 4, "x3"])
 def test_merged_tail_blocks_match_oracle(l2_n_major, split):
     # an expert's last pool block of at most 32 rows is computed by the tile
     # of the block before it (160 rows at most, one weight stream); both tile
     # orders (N-major also takes L2 tiles across XCDs) and the split phases
+    # (by workgroup budget, and on disjoint XCD sets: "x3")
     inp, ref = _merge_case()
-    run = G.Runner(inp, block_m=128, l2_n_major=l2_n_major, split_l2_cus=split)
+    kw = dict(split_l2_xcds=3) if split == "x3" else dict(split_l2_cus=split)
+    run = G.Runner(inp, block_m=128, l2_n_major=l2_n_major, **kw)
     try:
         assert run.forward() == 0
         err = _compare_all(inp, ref, run, f"merge l2_n_major {l2_n_major} split {split}")
@@ -400,3 +402,39 @@ def test_split_phases_reject_too_many_l2_cus():
     with pytest.raises(B.MegaMoEError) as ei:
         G.Runner(inp, split_l2_cus=40)
     assert ei.value.code == B.MEGA_MOE_ERR_INVALID_ARG
+    # every XCD for the L2 tiles leaves none for the L1 tiles
+    import torch
+    n_xcd = torch.cuda.get_device_properties(0).multi_processor_count // 32
+    with pytest.raises(B.MegaMoEError) as ei:
+        G.Runner(inp, split_l2_xcds=n_xcd)
+    assert ei.value.code == B.MEGA_MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ["ragged", "many_blocks", "skewed"])
+@pytest.mark.parametrize("l2_xcds", [1, 3, 6])
+def test_split_xcds_match_fused_and_oracle(name, l2_xcds):
+    # the L1 and L2 tiles on disjoint XCD sets (green-context partitions of
+    # whole dies, "PR357 Green-Context Split MegaMoE code review" 5.2): the
+    # same tiles and arithmetic as the fused kernel, so identical bits, for
+    # FP8 and MXFP4 weights; and the FP8 result against the oracle
+    for mx in (False, True):
+        if mx:
+            wl = dataclasses.replace(SMALL[name], name=name + "_mxfp4", weight_format="mxfp4")
+            inp, ref = S.make_inputs(wl), None
+        else:
+            inp, ref = _case(name)
+        outs = []
+        for split in (0, l2_xcds):
+            print(f"[{name} mx={mx}] split_l2_xcds {split}", flush=True)
+            run = G.Runner(inp, split_l2_xcds=split)
+            try:
+                assert run.forward() == 0
+                v = run.views(inp["x"].shape[0])
+                outs.append((run.y().copy(), v["l2_acts"].copy(), v["comb"].copy()))
+                if split and ref is not None:
+                    err = _compare_all(inp, ref, run, f"{name} split_l2_xcds {split}")
+                    print(f"{name} split_l2_xcds {split}: y rel frobenius {err:.2e}")
+            finally:
+                run.close()
+        for a, b in zip(*outs):
+            assert np.array_equal(a, b), (name, mx, l2_xcds)

@@ -74,12 +74,12 @@ def test_full_size_all_routes(name):
 def test_split_phases_full_decode_match_oracle():
     inp = S.make_inputs("decode")
     ref = moe.forward(inp)
-    for l2_cus in (8, 16):
-        print(f"[decode split {l2_cus}] GPU forward", flush=True)
-        run = G.Runner(inp, split_l2_cus=l2_cus)
+    for kw in (dict(split_l2_cus=8), dict(split_l2_cus=16), dict(split_l2_xcds=3)):
+        print(f"[decode {kw}] GPU forward", flush=True)
+        run = G.Runner(inp, **kw)
         try:
             assert run.forward() == 0
-            _compare_full(inp, ref, run, f"decode split_l2_cus {l2_cus}")
+            _compare_full(inp, ref, run, f"decode {kw}")
         finally:
             run.close()
 
