@@ -252,11 +252,13 @@ EDGE = {
 def test_edge_shapes_match_oracle(name):
     inp = S.make_inputs(EDGE[name])
     ref = moe.forward(inp)
-    for bm in (0, 64, 128):
-        run = G.Runner(inp, block_m=bm)
+    # every tile height, and the phases on disjoint XCD sets (one L2 XCD:
+    # one pool block or none per L1 XCD on the small batches)
+    for kw in (dict(block_m=0), dict(block_m=64), dict(block_m=128), dict(split_l2_xcds=1)):
+        run = G.Runner(inp, **kw)
         try:
             assert run.forward() == 0
-            _compare_all(inp, ref, run, f"{name} block_m {bm}")
+            _compare_all(inp, ref, run, f"{name} {kw}")
         finally:
             run.close()
 
