@@ -566,9 +566,10 @@ static int forward_impl(mega_moe_handle* h, int32_t T, const uint8_t* x, const f
     launch_dispatch(a, gather_blocks, stream);
     if (call >= 0) hipEventRecord(prof_event(h, call, 1), stream);
     if (h->split_stream[0]) {
-        // the L1 and L2 tiles as two concurrent kernels (disjoint workgroup
-        // budgets, or disjoint XCD sets), forked from and joined back into the
-        // caller's stream
+        // the L1 and L2 tiles as two concurrent kernels with disjoint workgroup
+        // budgets, forked from and joined back into the caller's stream (the
+        // split on disjoint XCD sets runs in the one launch below: its
+        // arguments carry the XCD roles)
         hipEventRecord(h->split_event[0], stream);
         for (int i = 0; i < 2; ++i) {
             hipStreamWaitEvent(h->split_stream[i], h->split_event[0], 0);

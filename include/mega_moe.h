@@ -179,7 +179,8 @@ int mega_moe_forward_mxfp4(mega_moe_handle* h, int32_t num_tokens,
  * routine.  Its workspace is a device array inside the library of
  * MEGA_MOE_NOALLOC_SCRATCH_BYTES (128 MiB), one per GPU, held from the first
  * use until the process ends.
- *   cfg         as for mega_moe_create; keep_pool and split_l2_cus must be 0.
+ *   cfg         as for mega_moe_create; keep_pool, split_l2_cus and
+ *               split_l2_xcds must be 0.
  *               num_tokens <= cfg->max_tokens.
  *   num_tokens  a call needs mega_moe_workspace_bytes(cfg with max_tokens =
  *               num_tokens) + 256 bytes of the array; a larger call returns
