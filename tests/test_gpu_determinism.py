@@ -20,6 +20,9 @@ from tests import gpu_util as G
 pytestmark = pytest.mark.gpu
 
 REPEATS = {"decode": 12, "mid": 12, "wide": 12, "prefill": 4}
+# the phases on disjoint XCD sets: every pool block's L1 output crosses dies
+# (write-back, mark, invalidation), the path where an ordering slip would show
+SPLIT_REPEATS = {"decode": 12, "mid": 8}
 
 
 def _digest(*arrays):
@@ -45,3 +48,24 @@ def test_repeat_bitwise(name):
         assert len(distinct) == 1, f"{name}: {len(distinct)} distinct results in {len(digests)} runs"
     finally:
         run.close()
+
+
+@pytest.mark.parametrize("name", list(SPLIT_REPEATS))
+def test_repeat_bitwise_split_xcds(name):
+    inp = S.make_inputs(name)
+    T = inp["x"].shape[0]
+    print(f"[{name} split_l2_xcds 3] {SPLIT_REPEATS[name]} forwards", flush=True)
+    runs = [G.Runner(inp), G.Runner(inp, split_l2_xcds=3)]
+    try:
+        assert runs[0].forward() == 0
+        v = runs[0].views(T, full=False)
+        fused = _digest(v["l2_acts"], v["l2_sf"], runs[0].y())
+        digests = []
+        for _ in range(SPLIT_REPEATS[name]):
+            assert runs[1].forward() == 0
+            v = runs[1].views(T, full=False)
+            digests.append(_digest(v["l2_acts"], v["l2_sf"], runs[1].y()))
+        assert set(digests) == {fused}, f"{name}: {len(set(digests))} distinct split results"
+    finally:
+        for r in runs:
+            r.close()
