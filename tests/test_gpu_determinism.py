@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 REPEATS = {"decode": 12, "mid": 12, "wide": 12, "prefill": 4}
 # the phases on disjoint XCD sets: every pool block's L1 output crosses dies
 # (write-back, mark, invalidation), the path where an ordering slip would show
-SPLIT_REPEATS = {"decode": 12, "mid": 8}
+SPLIT_REPEATS = {"decode": 12, "mid": 8, "prefill": 2}
 
 
 def _digest(*arrays):
