@@ -137,7 +137,7 @@ Layout make_layout(const mega_moe_config& c) {
     // the pool copies exist only when the configuration keeps the pool
     const int64_t pool_rows = c.keep_pool ? L.P_cap : 0;
     sz[L_L1ACTS] = pool_rows * H;
-    sz[L_L1SF] = (H / 128) * pool_rows * 4;
+    sz[L_L1SF] = (H / 128) * L.P_cap * 4;   // also the 128-row tiles' pool-ordered scales
     sz[L_L1W] = pool_rows * 4;
     sz[L_L2ACTS] = L.P_cap * I;
     sz[L_L2SF] = (I / 64) * L.P_cap * 4;

@@ -17,6 +17,9 @@
 //   moe_dispatch_scatter one workgroup per chunk: stable rank of every route
 //                        inside its expert (wave ballots), slot map and source
 //                        metadata
+// then, for the expert kernel's 128-row tiles,
+//   moe_pool_scales      the activation scales in pool order (one run per K
+//                        block), which those tiles read instead of gathering
 // and, with the pool kept, one more:
 //   moe_dispatch_gather  copy of the FP8 row, its scales and its top-k weight
 //                        into the pool row of every route
@@ -356,6 +359,36 @@ moe_dispatch_gather(MoeArgs a) {
     }
 }
 
+// The activation scales in pool order, for the 128-row tiles: l1_sf[kb, s] =
+// x_sf[t, kb] for pool row s holding a route of token t, 0 for padding rows
+// ("MegaMoE SM90 Implementation Design (Final)" 9.2: the pool keeps the
+// scales MN-major).  A 128-row L1 tile then reads a step's scales as one
+// contiguous run instead of one cache line per row, and the gather from x_sf
+// happens once per pool row instead of once per N block.  A workgroup
+// transposes POOL_SF_ROWS pool rows through LDS: it reads each row's scales
+// as one contiguous run of x_sf and writes each K block's run of rows as one
+// contiguous run of l1_sf.
+constexpr int POOL_SF_ROWS = 16;
+
+__global__ void __launch_bounds__(256)
+moe_pool_scales(MoeArgs a) {
+    __shared__ float tile[64 * POOL_SF_ROWS];          // [kb][row], H / 128 <= 64
+    const int kb_n = a.H / 128;
+    const int s0 = blockIdx.x * POOL_SF_ROWS;
+    const int rows = min(POOL_SF_ROWS, a.offsets[a.E] - s0);
+    if (rows <= 0) return;
+    for (int i = threadIdx.x; i < POOL_SF_ROWS * kb_n; i += blockDim.x) {
+        const int r = i / kb_n, kb = i - r * kb_n;
+        const int f = r < rows ? a.src[s0 + r] : -1;
+        tile[kb * POOL_SF_ROWS + r] = f >= 0 ? a.x_sf[(size_t)(f / a.k) * kb_n + kb] : 0.0f;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < POOL_SF_ROWS * kb_n; i += blockDim.x) {
+        const int kb = i / POOL_SF_ROWS, r = i - kb * POOL_SF_ROWS;
+        if (r < rows) a.l1_sf[(size_t)kb * a.P_cap + s0 + r] = tile[kb * POOL_SF_ROWS + r];
+    }
+}
+
 __global__ void __launch_bounds__(256) moe_clear_words(uint32_t* p, int n) {
     for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
 }
@@ -377,6 +410,11 @@ void launch_dispatch(const MoeArgs& a, int gather_blocks, hipStream_t stream) {
     // the pool copies are only for inspection (the expert kernel reads x)
     if (gather_blocks > 0)
         hipLaunchKernelGGL(moe_dispatch_gather, dim3(gather_blocks), dim3(256), 0, stream, a);
+    // 128-row tiles read the activation scales in pool order
+    if (a.block_m == 128) {
+        const int64_t blocks = (a.P_cap + POOL_SF_ROWS - 1) / POOL_SF_ROWS;
+        hipLaunchKernelGGL(moe_pool_scales, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    }
 }
 
 }  // namespace mega_moe

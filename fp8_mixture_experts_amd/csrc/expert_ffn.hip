@@ -466,11 +466,13 @@ struct Loader {
     // ra: activation rows (row_a bytes each), rb: weight rows (row_b bytes),
     // rs: activation scales, rw: UE8M0 scale rows of the weight rows (row_w
     // bytes; MXFP4 only).  L1 tiles (HALVES 1) gather: arow[n] is the row of
-    // x (and of x_sf) that tile row n reads, or a row past the end of ra / rs
-    // for the padding rows, which then load as zeros; the scales are then
-    // one float per row (row stride row_s bytes, step kb at byte 4 kb).  L2
-    // tiles read the pool in order (arow unused) and its pool-minor scales
-    // (row stride P).
+    // x that tile row n reads, or a row past the end of ra for the padding
+    // rows, which then load as zeros; their scales are one float per row:
+    // on 128-row tiles from the dispatch's pool-ordered copy (rs starts at
+    // the tile's first pool row, row stride 4 bytes, step kb at byte 4 P kb),
+    // else gathered from x_sf like the rows (row stride row_s bytes, step kb
+    // at byte 4 kb).  L2 tiles read the pool in order (arow unused) and its
+    // pool-minor scales (row stride P).
     // rows: the tile's rows; the activation rows of the extra slice load only
     // when it has some (a tile of at most PBM rows issues what a PBM-row
     // configuration would)
@@ -498,7 +500,13 @@ struct Loader {
             voff_b = n * row_b + 16 * ((lane & 7) ^ row_swz(n));
             bstep = 8 * C::NW * row_b;
         }
-        if constexpr (HALVES == 1) {
+        if constexpr (HALVES == 1 && MS == 4) {
+            // one scale per lane: rows [w*BM/NW, (w+1)*BM/NW) of the tile, from
+            // the dispatch's pool-ordered copy (one contiguous run per step)
+            const int n = w * (C::BM / C::NW) + min(lane, C::BM / C::NW - 1);
+            sf_voff = n * 4;
+            sf_step = P * 4;
+        } else if constexpr (HALVES == 1) {
             // one scale per lane: rows [w*BM/NW, (w+1)*BM/NW) of the tile
             const int n = w * (C::BM / C::NW) + min(lane, C::BM / C::NW - 1);
             sf_voff = arow[n] * row_s;
@@ -673,7 +681,9 @@ __device__ __forceinline__ void l1_tile(const MoeArgs& a, const Lds<MS, BNT, WF>
     const Loader<MS, BNT, 1, WF> ld(
         make_rsrc(a.x, (uint32_t)((size_t)a.T * H)),
         make_rsrc(a.w1 + wrow0 * row_b, (uint32_t)(BN * row_b)), H, row_b,
-        make_rsrc(a.x_sf, (uint32_t)((size_t)a.T * KB * 4)), (int)P,
+        MS == 4 ? make_rsrc(a.l1_sf + row0, (uint32_t)(((size_t)(KB - 1) * P + valid) * 4))
+                : make_rsrc(a.x_sf, (uint32_t)((size_t)a.T * KB * 4)),
+        (int)P,
         make_rsrc(C::MX ? a.w1_e8 + wrow0 * (H / 32) : nullptr, C::MX ? (uint32_t)(BN * (H / 32)) : 0u),
         H / 32, valid, lds.tile() + 4, KB * 4);
     // MXFP4: smallest and largest block scale this lane converted (reported

@@ -76,7 +76,8 @@ struct MoeArgs {
     int32_t* chunk_hist;  // [num_chunks, E]
     int32_t* chunk_base;  // [num_chunks, E]
     uint8_t* l1_acts;     // [P_cap, H]  pool copy of the routed rows (kept pool only)
-    float* l1_sf;         // [H/128, P_cap]  their scales (kept pool only)
+    float* l1_sf;         // [H/128, P_cap]  their scales (with the kept pool; for
+                          //                 128-row tiles always, written by the dispatch)
     float* l1_w;          // [P_cap]  their top-k weights (kept pool only)
     uint8_t* l2_acts;     // [P_cap, I]
     float* l2_sf;         // [I/64, P_cap]
